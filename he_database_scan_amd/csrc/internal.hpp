@@ -1,0 +1,71 @@
+// internal.hpp -- launch interfaces between the C-ABI layer (pirscan_api.hip)
+// and the gfx950 kernels.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pirscan {
+
+constexpr int kMaxLimbs = 8;
+
+// Per-limb constants precomputed on the host for the RowSel kernels.
+struct LimbConsts {
+  uint32_t q[kMaxLimbs];      // modulus
+  uint32_t c[kMaxLimbs];      // 2^32 mod q: folds hi*2^32 + lo into hi*c + lo
+  uint64_t mu[kMaxLimbs];     // floor((2^64 - 1) / q): Barrett constant for the final reduction
+};
+
+struct RowselLaunch {
+  const uint32_t* ct;      // [m][D0][P]
+  const uint32_t* dbt;     // [P][D0][D1]
+  uint32_t* out;           // [m][D1][P]
+  uint64_t P;
+  uint32_t N, D0, D1, m;
+  uint32_t fold;           // products accumulated between two folds (>= 1)
+  LimbConsts lc;
+};
+
+// R1: [D0*D1][P] -> [P][D0*D1] word transpose.
+hipError_t launch_layout_db(const uint32_t* src, uint32_t* dst, uint64_t X, uint64_t P,
+                            hipStream_t stream);
+
+// R2-R4: the modular GEMM scan.
+hipError_t launch_rowsel(const RowselLaunch& a, hipStream_t stream);
+
+// Products of (q-1)^2 that fit between folds for modulus q (host helper).
+uint32_t rowsel_fold_period(uint32_t q);
+
+// ---- scalar-HE ---------------------------------------------------------
+
+struct ScalarPlan {
+  bool fast;          // aligned fast paths (K % 16 == 0, 16-byte aligned db)
+  bool mfma;          // B > 1 on int8 MFMA
+  uint32_t bgroup;    // columns per MFMA pass (<= 32)
+  uint32_t bpad;      // bgroup rounded up to 16
+  uint64_t kblock;    // split-K block (k per partial sum)
+  uint64_t nkb;       // number of k blocks
+  uint64_t kpad;      // nkb * kblock
+  size_t digit_bytes; // digit planes
+  size_t part_bytes;  // split-K partial sums (0 when nkb == 1)
+  size_t total_bytes; // workspace requirement
+};
+
+bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPlan* plan);
+
+hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out, uint64_t M,
+                         uint64_t K, uint32_t B, const ScalarPlan& plan, void* workspace,
+                         hipStream_t stream);
+
+// Maps a hardware workgroup id to a logical tile id so that consecutive
+// logical tiles run on the same XCD (gfx950 dispatches workgroups round-robin
+// over its 8 XCDs, each with a private L2).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t pid, uint32_t num) {
+  constexpr uint32_t kXcds = 8;
+  const uint32_t xcd = pid % kXcds, local = pid / kXcds;
+  const uint32_t per = num / kXcds, rem = num % kXcds;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace pirscan

@@ -1,0 +1,413 @@
+// scalar.hip -- the scalar-HE (Regev/LWE) database product on gfx950:
+//
+//     out[i][b] = sum_k sext32(db[i][k]) * query[k][b]   (mod 2^32)
+//
+// (VIPIR section 2.5: the batched SimplePIR online step is one D1 x B x D0
+// INT8-INT32 GEMM; section 4: with a 2^32 ciphertext modulus the reduction is
+// free.)
+//
+// Every query word is split into four signed int8 digits s_j in [-128, 127]
+// with sum_j s_j 2^(8j) == word (mod 2^32) (VIPIR section 4.1 splits the INT32
+// operand into four INT8 matrices and recombines with shifts; the signed form
+// fits the signed int8 x int8 datapaths of gfx950).  The split is unique, and
+// the whole digit vector of a word w is the byte-wise view of
+// (w + 0x80808080) ^ 0x80808080: adding 128 to every byte position with full
+// carries moves each digit into [0, 255], flipping each byte's top bit moves
+// it back to [-128, 127].
+//
+//  * B == 1 (S2): HBM-bound GEMV.  Each wavefront keeps the digits of one
+//    4096-wide k-block in registers and streams 64 DB rows of that block with
+//    128-bit loads, one v_dot4 (4 int8 products) per DB dword per digit plane.
+//    Split-K partial sums (one per row and k-block) are added mod 2^32.
+//  * B  > 1 (S3): int8 MFMA (v_mfma_i32_16x16x64_i8).  DB rows are the A
+//    operand, the 4*B digit columns the B operand; int32 accumulation never
+//    overflows because a k-block is at most 2^14 long (|sum| <= 2^28).  The
+//    epilogue recombines the four digit planes with shifts, mod 2^32.
+#include <hip/hip_runtime.h>
+
+#include "internal.hpp"
+
+namespace pirscan {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGemvJ = 4;                          // 16-byte loads per lane per row
+constexpr uint64_t kGemvKBlock = 64 * 16 * kGemvJ;  // 4096
+constexpr int kGemvRowsPerWave = 64;
+constexpr int kGemvRowBatch = 4;
+constexpr uint64_t kMfmaKBlockMax = 16384;
+constexpr int kMfmaRowTiles = 4;                   // 4 x 16 rows per wavefront
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t signed_digits_word(uint32_t w) {
+  return (w + 0x80808080u) ^ 0x80808080u;
+}
+
+// ---------------------------------------------------------------------------
+// S1, GEMV layout: for every group g of 4 consecutive k, 4 dwords (one per
+// digit plane j); byte t of dword j is digit j of query[4g + t].  Zero past K.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void split_gemv_kernel(const uint32_t* __restrict__ query,
+                                                              uint32_t* __restrict__ dig,
+                                                              uint64_t K, uint64_t groups, uint32_t ldq,
+                                                              uint32_t col) {
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g < groups; g += stride) {
+    uint32_t d[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint64_t k = 4 * g + t;
+      d[t] = k < K ? signed_digits_word(query[k * ldq + col]) : 0u;
+    }
+    // plane j gathers byte j of the four words
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      p[j] = ((d[0] >> (8 * j)) & 0xFFu) | (((d[1] >> (8 * j)) & 0xFFu) << 8) |
+             (((d[2] >> (8 * j)) & 0xFFu) << 16) | (((d[3] >> (8 * j)) & 0xFFu) << 24);
+    uint4 o;
+    o.x = p[0]; o.y = p[1]; o.z = p[2]; o.w = p[3];
+    reinterpret_cast<uint4*>(dig)[g] = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S2: GEMV.  Workgroup = 4 wavefronts x 64 rows of one k-block.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t xor_sum_tail(uint32_t v, int from) {
+  for (int off = from; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const int8_t* __restrict__ db,
+                                                        const uint32_t* __restrict__ dig,
+                                                        uint32_t* __restrict__ dst, uint64_t M,
+                                                        uint64_t K, uint64_t nkb) {
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const uint64_t kb = wg % nkb, rb = wg / nkb;
+  const uint64_t row0 = (rb * (kThreads / 64) + wave) * kGemvRowsPerWave;
+  if (row0 >= M) return;  // no barriers below
+  const uint64_t rows = (M - row0) < (uint64_t)kGemvRowsPerWave ? (M - row0) : kGemvRowsPerWave;
+
+  // digits of this lane's 16*J k values: [t][u][j]
+  uint32_t dg[kGemvJ][4][4];
+  bool chunk_on[kGemvJ];
+#pragma unroll
+  for (int t = 0; t < kGemvJ; ++t) {
+    const uint64_t kc = kb * kGemvKBlock + (uint64_t)(t * 64 + lane) * 16;
+    chunk_on[t] = kc < K;
+    const uint4* src = reinterpret_cast<const uint4*>(dig + kc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 v = src[u];
+      dg[t][u][0] = v.x; dg[t][u][1] = v.y; dg[t][u][2] = v.z; dg[t][u][3] = v.w;
+    }
+  }
+
+  const int8_t* base = db + row0 * K + kb * kGemvKBlock + (uint64_t)lane * 16;
+  uint32_t result = 0;
+  for (uint64_t r = 0; r < rows; r += kGemvRowBatch) {
+    uint32_t s[kGemvRowBatch];
+    uint4 v[kGemvRowBatch][kGemvJ];
+#pragma unroll
+    for (int rr = 0; rr < kGemvRowBatch; ++rr) {
+      const bool row_on = r + rr < rows;
+#pragma unroll
+      for (int t = 0; t < kGemvJ; ++t) {
+        v[rr][t] = (row_on && chunk_on[t])
+                       ? *reinterpret_cast<const uint4*>(base + (r + rr) * K + t * 1024)
+                       : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < kGemvRowBatch; ++rr) {
+      int acc[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < kGemvJ; ++t) {
+        const uint32_t w[4] = {v[rr][t].x, v[rr][t].y, v[rr][t].z, v[rr][t].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[j] = __builtin_amdgcn_sdot4((int)w[u], (int)dg[t][u][j], acc[j], false);
+      }
+      s[rr] = (uint32_t)acc[0] + ((uint32_t)acc[1] << 8) + ((uint32_t)acc[2] << 16) +
+              ((uint32_t)acc[3] << 24);
+    }
+    // Reduce 4 rows over 64 lanes with 7 cross-lane adds: two merge steps
+    // leave row (2*bit4 + bit5) of the lane's index in each lane, then a
+    // 16-lane butterfly finishes every row.
+    const bool hi32 = lane & 32, hi16 = lane & 16;
+    const uint32_t a01 = (hi32 ? s[1] : s[0]) + __shfl_xor(hi32 ? s[0] : s[1], 32, 64);
+    const uint32_t a23 = (hi32 ? s[3] : s[2]) + __shfl_xor(hi32 ? s[2] : s[3], 32, 64);
+    uint32_t t = (hi16 ? a23 : a01) + __shfl_xor(hi16 ? a01 : a23, 16, 64);
+    t = xor_sum_tail(t, 8);
+    const uint32_t sum0 = __shfl(t, 0, 64), sum1 = __shfl(t, 32, 64);
+    const uint32_t sum2 = __shfl(t, 16, 64), sum3 = __shfl(t, 48, 64);
+    const uint64_t lr = lane;
+    if (lr == r) result = sum0;
+    if (lr == r + 1) result = sum1;
+    if (lr == r + 2) result = sum2;
+    if (lr == r + 3) result = sum3;
+  }
+  if (lane < rows) dst[kb * M + row0 + lane] = result;
+}
+
+// ---------------------------------------------------------------------------
+// S1, MFMA layout: for every 16-k group and digit column c = j*bpad + b, 16
+// bytes (digit j of query[k][b] for the 16 k of the group).  Zero for k >= K
+// and for padding columns b >= bgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void split_mfma_kernel(const uint32_t* __restrict__ query,
+                                                              uint8_t* __restrict__ dig,
+                                                              uint64_t K, uint64_t k16_groups,
+                                                              uint32_t bpad, uint32_t bgroup,
+                                                              uint32_t ldq, uint32_t col0) {
+  const uint64_t total = k16_groups * bpad;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t e = (uint64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const uint64_t g = e / bpad;
+    const uint32_t b = (uint32_t)(e % bpad);
+    uint32_t plane[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) plane[j][w] = 0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint64_t k = g * 16 + t;
+      const uint32_t d = (k < K && b < bgroup) ? signed_digits_word(query[k * ldq + col0 + b]) : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) plane[j][t / 4] |= ((d >> (8 * j)) & 0xFFu) << (8 * (t % 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 o;
+      o.x = plane[j][0]; o.y = plane[j][1]; o.z = plane[j][2]; o.w = plane[j][3];
+      reinterpret_cast<uint4*>(dig)[g * 4 * bpad + (uint64_t)j * bpad + b] = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S3: int8 MFMA GEMM.  Workgroup = 4 wavefronts x 64 rows of one k-block.
+// NT = 16-column tiles = 4 * bpad / 16.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(kThreads) void mfma_kernel(const int8_t* __restrict__ db,
+                                                        const uint8_t* __restrict__ dig,
+                                                        uint32_t* __restrict__ dst, uint64_t M,
+                                                        uint64_t K, uint64_t kblock, uint64_t nkb,
+                                                        uint64_t row_blocks, uint32_t bgroup,
+                                                        uint64_t ldd, uint32_t dcol0) {
+  constexpr int HT = NT / 4;  // column tiles per digit plane
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const uint64_t kb = wg / row_blocks, rb = wg % row_blocks;
+  const uint64_t row0 = (rb * (kThreads / 64) + wave) * (16 * kMfmaRowTiles);
+  if (row0 >= M) return;  // no barriers below
+  const uint32_t li = lane % 16, lg = lane / 16;
+
+  v4i acc[kMfmaRowTiles][NT];
+#pragma unroll
+  for (int rt = 0; rt < kMfmaRowTiles; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[rt][ct] = v4i{0, 0, 0, 0};
+
+  bool row_on[kMfmaRowTiles];
+  const int8_t* arow[kMfmaRowTiles];
+#pragma unroll
+  for (int rt = 0; rt < kMfmaRowTiles; ++rt) {
+    const uint64_t row = row0 + rt * 16 + li;
+    row_on[rt] = row < M;
+    arow[rt] = db + (row_on[rt] ? row : 0) * K;
+  }
+  const uint64_t kbeg = kb * kblock;
+  const uint64_t kend = kbeg + kblock;  // digits are zero-padded up to nkb*kblock
+  const uint32_t dcols = 4 * NT * 4;    // 4 * bpad digit columns
+  for (uint64_t kk = kbeg; kk < kend; kk += 64) {
+    const uint64_t kc = kk + 16 * lg;
+    const bool k_on = kc < K;
+    v4i a[kMfmaRowTiles];
+#pragma unroll
+    for (int rt = 0; rt < kMfmaRowTiles; ++rt)
+      a[rt] = (row_on[rt] && k_on) ? *reinterpret_cast<const v4i*>(arow[rt] + kc) : v4i{0, 0, 0, 0};
+    const v4i* bsrc = reinterpret_cast<const v4i*>(dig) + (kc / 16) * dcols + li;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const v4i bf = bsrc[ct * 16];
+#pragma unroll
+      for (int rt = 0; rt < kMfmaRowTiles; ++rt)
+        acc[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[rt], bf, acc[rt][ct], 0, 0, 0);
+    }
+  }
+
+  // D element i of lane l is (row 4*(l/16) + i, column l%16) of the tile.
+#pragma unroll
+  for (int rt = 0; rt < kMfmaRowTiles; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t row = row0 + rt * 16 + 4 * lg + i;
+      if (row >= M) continue;
+#pragma unroll
+      for (int h = 0; h < HT; ++h) {
+        const uint32_t b = h * 16 + li;
+        if (b >= bgroup) continue;
+        uint32_t v = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v += (uint32_t)acc[rt][j * HT + h][i] << (8 * j);
+        if (nkb == 1) dst[row * ldd + dcol0 + b] = v;
+        else dst[(kb * M + row) * bgroup + b] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduction: out[row*ldo + col0 + b] = sum_kb part[(kb*M + row)*cols + b]
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void reduce_kernel(const uint32_t* __restrict__ part,
+                                                          uint32_t* __restrict__ out, uint64_t M,
+                                                          uint32_t cols, uint64_t nkb, uint64_t ldo,
+                                                          uint32_t col0) {
+  const uint64_t total = M * cols;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t e = (uint64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    uint32_t s = 0;
+    for (uint64_t kb = 0; kb < nkb; ++kb) s += part[kb * total + e];
+    const uint64_t row = e / cols;
+    const uint32_t b = (uint32_t)(e % cols);
+    out[row * ldo + col0 + b] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Any shape / alignment: one thread per output, byte loads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void generic_kernel(const int8_t* __restrict__ db,
+                                                           const uint32_t* __restrict__ query,
+                                                           uint32_t* __restrict__ out, uint64_t M,
+                                                           uint64_t K, uint32_t B) {
+  const uint64_t total = M * B;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t e = (uint64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const uint64_t row = e / B;
+    const uint32_t b = (uint32_t)(e % B);
+    uint32_t s = 0;
+    for (uint64_t k = 0; k < K; ++k) s += (uint32_t)(int32_t)db[row * K + k] * query[k * B + b];
+    out[e] = s;
+  }
+}
+
+uint32_t grid_for(uint64_t items, uint64_t cap = 1u << 20) {
+  uint64_t g = (items + kThreads - 1) / kThreads;
+  if (g > cap) g = cap;
+  return (uint32_t)(g ? g : 1);
+}
+
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+uint64_t align_up(uint64_t a, uint64_t b) { return ceil_div(a, b) * b; }
+
+template <int NT>
+hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint64_t M, uint64_t K,
+                       const ScalarPlan& pl, uint32_t bgroup, uint64_t ldd, uint32_t dcol0,
+                       hipStream_t stream) {
+  const uint64_t rows_per_wg = (kThreads / 64) * 16 * kMfmaRowTiles;
+  const uint64_t row_blocks = ceil_div(M, rows_per_wg);
+  const uint64_t grid = row_blocks * pl.nkb;
+  if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mfma_kernel<NT>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, db, dig, dst,
+                     M, K, pl.kblock, pl.nkb, row_blocks, bgroup, ldd, dcol0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPlan* p) {
+  *p = ScalarPlan{};
+  if (M == 0 || K == 0 || B == 0) return false;
+  if (B > (1u << 20)) return false;
+  const unsigned __int128 lim = (unsigned __int128)1 << 62;
+  if ((unsigned __int128)M * K > lim || (unsigned __int128)M * B * 4 > lim ||
+      (unsigned __int128)K * B * 4 > lim)
+    return false;
+  p->fast = (K % 16 == 0) && (db_addr % 16 == 0);
+  if (!p->fast) return true;  // generic kernel, no workspace
+  if (B == 1) {
+    p->mfma = false;
+    p->bgroup = 1;
+    p->bpad = 1;
+    p->kblock = kGemvKBlock;
+    p->nkb = ceil_div(K, p->kblock);
+    p->kpad = p->nkb * p->kblock;
+    p->digit_bytes = p->kpad * 4;  // 4 digit planes x 1 byte per k
+    p->part_bytes = p->nkb > 1 ? p->nkb * M * 4 : 0;
+  } else {
+    p->mfma = true;
+    p->bgroup = B < 32 ? B : 32;
+    p->bpad = (uint32_t)align_up(p->bgroup, 16);
+    p->kblock = K > kMfmaKBlockMax ? kMfmaKBlockMax : align_up(K, 64);
+    p->nkb = ceil_div(K, p->kblock);
+    p->kpad = p->nkb * p->kblock;
+    p->digit_bytes = p->kpad * 4 * p->bpad;
+    p->part_bytes = p->nkb > 1 ? p->nkb * M * p->bgroup * 4 : 0;
+  }
+  p->total_bytes = align_up(p->digit_bytes, 256) + p->part_bytes;
+  return true;
+}
+
+hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out, uint64_t M,
+                         uint64_t K, uint32_t B, const ScalarPlan& pl, void* workspace,
+                         hipStream_t stream) {
+  if (!pl.fast) {
+    hipLaunchKernelGGL(generic_kernel, dim3(grid_for(M * B)), dim3(kThreads), 0, stream, db, query,
+                       out, M, K, B);
+    return hipGetLastError();
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* part = reinterpret_cast<uint32_t*>(ws + align_up(pl.digit_bytes, 256));
+  hipError_t e;
+  if (!pl.mfma) {
+    uint32_t* dig = reinterpret_cast<uint32_t*>(ws);
+    const uint64_t groups = pl.kpad / 4;
+    hipLaunchKernelGGL(split_gemv_kernel, dim3(grid_for(groups)), dim3(kThreads), 0, stream, query,
+                       dig, K, groups, 1u, 0u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint64_t row_blocks = ceil_div(M, (kThreads / 64) * kGemvRowsPerWave);
+    const uint64_t grid = row_blocks * pl.nkb;
+    if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    uint32_t* dst = pl.nkb > 1 ? part : out;
+    hipLaunchKernelGGL(gemv_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, db, dig, dst, M,
+                       K, pl.nkb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (pl.nkb > 1) {
+      hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M)), dim3(kThreads), 0, stream, part, out, M, 1u,
+                         pl.nkb, 1ull, 0u);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  uint8_t* dig = ws;
+  for (uint32_t c0 = 0; c0 < B; c0 += pl.bgroup) {
+    const uint32_t bg = (B - c0) < pl.bgroup ? (B - c0) : pl.bgroup;
+    const uint32_t bpad = (uint32_t)align_up(bg, 16);
+    const uint64_t k16 = pl.kpad / 16;
+    hipLaunchKernelGGL(split_mfma_kernel, dim3(grid_for(k16 * bpad)), dim3(kThreads), 0, stream, query,
+                       dig, K, k16, bpad, bg, B, c0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint32_t* dst = pl.nkb > 1 ? part : out;
+    if (bpad == 16) e = launch_mfma<4>(db, dig, dst, M, K, pl, bg, B, c0, stream);
+    else e = launch_mfma<8>(db, dig, dst, M, K, pl, bg, B, c0, stream);
+    if (e != hipSuccess) return e;
+    if (pl.nkb > 1) {
+      hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M * bg)), dim3(kThreads), 0, stream, part, out, M,
+                         bg, pl.nkb, (uint64_t)B, c0);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace pirscan

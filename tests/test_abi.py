@@ -1,0 +1,131 @@
+"""The C-ABI library (no GPU needed): it loads, exports every function that
+include/pirscan.h declares, and rejects bad arguments before touching the
+device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from he_database_scan_amd import pirscan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pirscan.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pirscan_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("pirscan_layout_db", "pirscan_rowsel_modgemm", "pirscan_scalar_gemm_u32",
+                 "pirscan_scalar_workspace_bytes", "pirscan_layout_db_bytes", "pirscan_strerror",
+                 "pirscan_version", "pirscan_last_device_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(pirscan.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_strerror():
+    assert pirscan.version() == 10000
+    assert pirscan.strerror(0) == "ok"
+    assert "invalid" in pirscan.strerror(-1)
+    assert "gfx950" in pirscan.strerror(-3)
+
+
+Q3 = [536813569, 536690689, 536641537]
+
+
+def test_layout_bytes_and_invalid_shapes():
+    s = pirscan.RowselShape.make(4096, Q3, 1024, 1024)
+    assert pirscan.layout_db_bytes(s) == 51539607552  # 48 GiB
+    bad = [pirscan.RowselShape.make(0, Q3, 4, 4), pirscan.RowselShape.make(4, Q3, 0, 4),
+           pirscan.RowselShape.make(4, Q3, 4, 0), pirscan.RowselShape.make(4, [1], 4, 4),
+           pirscan.RowselShape.make(4, [0, 7], 4, 4)]
+    for b in bad:
+        assert pirscan.layout_db_bytes(b) == 0
+    b = pirscan.RowselShape.make(4, Q3, 4, 4)
+    b.R = 9
+    assert pirscan.layout_db_bytes(b) == 0
+
+
+def test_page_size_identities():
+    """Sizes the pages print fix the layout conventions: a ciphertext is m=2
+    polynomials x R limbs x N points of 4 bytes (VIPIR 96 KiB / 48 KiB); GPIR's
+    a-polynomial is 4N points x 32 bit."""
+    sizes = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "page_sizes.txt")):
+        if line.strip() and not line.startswith("#"):
+            name, val = line.split()[:2]
+            sizes[name] = int(val)
+    N = 4096
+    ct_shape = pirscan.RowselShape.make(N, Q3, 1, 1)      # one DB point set: P = 3N
+    assert 2 * ct_shape.P * 4 == sizes["rlwe_ct_rns3_n4096"]   # ct [m=2][D0=1][P]
+    assert ct_shape.P * 4 == sizes["poly_rns3_n4096"]
+    gp = pirscan.RowselShape.make(N, [536813569] * 4, 1, 1)  # GPIR's 4N points
+    assert gp.P * 4 == sizes["gpir_a_poly_4n_n4096"]
+    assert 2 * gp.P * 4 == sizes["gpir_ct_4n_n4096"]
+    assert (1 << 16) * 4 == sizes["scalar_query_d0_65536"]
+
+
+def test_scalar_workspace_sizes():
+    # B=1: 4 digit bytes per k (k padded to 4096) + split-K partials
+    assert pirscan.scalar_workspace_bytes(32768, 32768, 1) == 32768 * 4 + 8 * 32768 * 4
+    assert pirscan.scalar_workspace_bytes(10, 4096, 1) == 4096 * 4          # one k-block: no partials
+    # B=8 (one MFMA pass, 16 padded digit columns x 4 planes)
+    assert pirscan.scalar_workspace_bytes(32768, 32768, 8) == 32768 * 64 + 2 * 32768 * 8 * 4
+    assert pirscan.scalar_workspace_bytes(0, 16, 1) == 0
+    assert pirscan.scalar_workspace_bytes(5, 17, 1) == 0                    # generic path
+
+
+def _call_rowsel(shape, m, ct, db, out):
+    L = pirscan.lib()
+    return L.pirscan_rowsel_modgemm(ctypes.byref(shape) if shape is not None else None, m,
+                                    ctypes.c_void_p(ct), ctypes.c_void_p(db), ctypes.c_void_p(out), None)
+
+
+def test_rowsel_rejects_bad_arguments_without_a_device():
+    s = pirscan.RowselShape.make(8, Q3, 4, 4)
+    A, B, C = 1 << 20, 1 << 30, 1 << 40  # fake, never dereferenced
+    assert _call_rowsel(None, 2, A, B, C) == pirscan.EINVAL
+    assert _call_rowsel(s, 0, A, B, C) == pirscan.EINVAL
+    assert _call_rowsel(s, 2, 0, B, C) == pirscan.EINVAL
+    assert _call_rowsel(s, 2, A, 0, C) == pirscan.EINVAL
+    assert _call_rowsel(s, 2, A, B, 0) == pirscan.EINVAL
+    assert _call_rowsel(s, 2, A, B, A + 4) == pirscan.EINVAL      # out overlaps ct
+    assert _call_rowsel(s, 2, A, B, B + 64) == pirscan.EINVAL     # out overlaps db
+    bad = pirscan.RowselShape.make(8, [1], 4, 4)
+    assert _call_rowsel(bad, 2, A, B, C) == pirscan.EINVAL
+    L = pirscan.lib()
+    assert L.pirscan_layout_db(ctypes.byref(s), ctypes.c_void_p(A), ctypes.c_void_p(A + 16), None) == pirscan.EINVAL
+
+
+def test_scalar_rejects_bad_arguments_without_a_device():
+    L = pirscan.lib()
+    A, B, C, W = 1 << 20, 1 << 30, 1 << 40, 1 << 44
+    f = lambda db, q, o, M, K, Bq, w, wb: L.pirscan_scalar_gemm_u32(
+        ctypes.c_void_p(db), ctypes.c_void_p(q), ctypes.c_void_p(o), M, K, Bq, ctypes.c_void_p(w), wb, None)
+    need = pirscan.scalar_workspace_bytes(64, 8192, 1)
+    assert f(0, B, C, 64, 8192, 1, W, need) == pirscan.EINVAL
+    assert f(A, B, C, 0, 8192, 1, W, need) == pirscan.EINVAL
+    assert f(A, B, C, 64, 8192, 0, W, need) == pirscan.EINVAL
+    assert f(A, B, C, 64, 8192, 1, W, need - 1) == pirscan.EINVAL     # workspace too small
+    assert f(A, B, C, 64, 8192, 1, 0, need) == pirscan.EINVAL          # no workspace
+    assert f(A, B, C, 64, 8192, 1, W + 4, need) == pirscan.EINVAL      # misaligned workspace
+    assert f(A, B, A + 8, 64, 8192, 1, W, need) == pirscan.EINVAL      # out overlaps db
+    assert f(A, B, C, 64, 8192, 1, B + 16, need) == pirscan.EINVAL     # workspace overlaps query
+    assert f(A, B, C, 1 << 40, 1 << 40, 1, W, need) == pirscan.EINVAL  # size overflow
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(pirscan, "LIB_PATH", "/nonexistent/libpirscan.so")
+    monkeypatch.setattr(pirscan, "_lib", None)
+    with pytest.raises(RuntimeError):
+        pirscan.version()

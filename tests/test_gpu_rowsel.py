@@ -1,0 +1,161 @@
+"""RowSel on the GPU through the C ABI, bit-exact against the oracle.
+
+Element-by-element at sizes the oracle finishes in seconds (several
+wavefront slices, ragged column / k tails, every row-group width and every
+fold period); sampled points at the full 3 GiB and 48 GiB configurations."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from he_database_scan_amd import pirscan
+from tests.gpu_util import MED_Q, TINY_Q, empty_u32, release, say, to_dev_u32, to_host_u32
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(ct, db, N, q):
+    m, D0, P = ct.shape
+    D1 = db.shape[1]
+    shape = pirscan.RowselShape.make(N, q, D0, D1)
+    d_db = to_dev_u32(db)
+    d_dbt = empty_u32(db.shape)
+    pirscan.layout_db(shape, d_db, d_dbt)
+    d_out = empty_u32((m, D1, P))
+    pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out)
+    return to_host_u32(d_out)
+
+
+def rand_res(rng, shape, N, q):
+    qv = np.asarray(q, dtype=np.uint64)[np.arange(shape[-1]) // N]
+    return (rng.integers(0, 1 << 63, size=shape, dtype=np.uint64) % qv).astype(np.uint32)
+
+
+def test_tiny_config_full():
+    N, m, D0, D1 = 256, 2, 16, 8
+    P = 2 * N
+    say("rowsel tiny")
+    ct = synth.residue_array(1, synth.STREAM_ROWSEL_CT, (m, D0, P), N, TINY_Q)
+    db = synth.residue_array(1, synth.STREAM_ROWSEL_DB, (D0, D1, P), N, TINY_Q)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, TINY_Q), oracle.rowsel(ct, db, N, TINY_Q))
+
+
+def test_tiny_one_hot_rows_and_all_max():
+    N, m, D0, D1 = 256, 2, 16, 8
+    P = 2 * N
+    db = synth.residue_array(1, synth.STREAM_ROWSEL_DB, (D0, D1, P), N, TINY_Q)
+    shape = pirscan.RowselShape.make(N, TINY_Q, D0, D1)
+    d_dbt = empty_u32(db.shape)
+    pirscan.layout_db(shape, to_dev_u32(db), d_dbt)
+    d_out = empty_u32((m, D1, P))
+    for k in range(D0):
+        ct = np.zeros((m, D0, P), dtype=np.uint32)
+        ct[:, k, :] = 1
+        pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out)
+        got = to_host_u32(d_out)
+        for mi in range(m):
+            np.testing.assert_array_equal(got[mi], db[k])
+    qv = np.asarray(TINY_Q, dtype=np.uint32)[np.arange(P) // N]
+    ctm = np.broadcast_to(qv - 1, (m, D0, P)).copy()
+    dbm = np.broadcast_to(qv - 1, (D0, D1, P)).copy()
+    got = run_gpu(ctm, dbm, N, TINY_Q)
+    assert (got == (D0 % qv)[None, None, :]).all()       # (q-1)^2 == 1: out = D0 mod q
+    np.testing.assert_array_equal(got, oracle.rowsel(ctm, dbm, N, TINY_Q))
+
+
+# (m, D0, D1): every row-group width (2/4/8/16/32 and a multi-pass m), the
+# 128/64/32-bit column paths, ragged column slices and k tails that cross the
+# LDS chunk and the fold period.
+SHAPES = [(2, 33, 256), (1, 7, 8), (3, 40, 300), (4, 64, 512), (6, 17, 258), (8, 65, 1024),
+          (12, 9, 130), (16, 70, 256), (32, 66, 128), (34, 5, 129), (2, 1, 1), (2, 1100, 64)]
+
+
+@pytest.mark.parametrize("m,D0,D1", SHAPES)
+def test_multi_tile_shapes_full(m, D0, D1):
+    rng = np.random.default_rng(m * 10000 + D0 * 100 + D1)
+    N, q = 16, MED_Q
+    P = N * len(q)
+    say(f"rowsel m={m} D0={D0} D1={D1} P={P}")
+    ct = rand_res(rng, (m, D0, P), N, q)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))
+
+
+@pytest.mark.parametrize("q", [[4294967291, 4294967279], [2147483659, 3221225473], [65537, 2],
+                               [3, 1073741827], [TINY_Q[0], MED_Q[0]]])
+def test_fold_periods_and_extreme_moduli(q):
+    """Moduli from 2 to just under 2^32 select every fold period (1..32);
+    all-(q-1) inputs are the 64-bit accumulator's worst case."""
+    rng = np.random.default_rng(q[0] % 1000)
+    N, m, D0, D1 = 8, 2, 97, 260
+    P = N * len(q)
+    say(f"rowsel moduli {q}")
+    ct = rand_res(rng, (m, D0, P), N, q)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))
+    qv = np.asarray(q, dtype=np.uint32)[np.arange(P) // N]
+    ctm = np.broadcast_to(qv - 1, (m, D0, P)).copy()
+    dbm = np.broadcast_to(qv - 1, (D0, D1, P)).copy()
+    np.testing.assert_array_equal(run_gpu(ctm, dbm, N, q), oracle.rowsel(ctm, dbm, N, q))
+
+
+def test_repeat_runs_identical():
+    rng = np.random.default_rng(1)
+    N, m, D0, D1 = 16, 2, 50, 512
+    ct = rand_res(rng, (m, D0, 3 * N), N, MED_Q)
+    db = rand_res(rng, (D0, D1, 3 * N), N, MED_Q)
+    a = run_gpu(ct, db, N, MED_Q)
+    b = run_gpu(ct, db, N, MED_Q)
+    np.testing.assert_array_equal(a, b)
+
+
+def sampled_full_size(seed, D0, D1, m, points, ct_stream=synth.STREAM_ROWSEL_CT):
+    """Full-size config synthesised on the device; the oracle regenerates the
+    inputs of the sampled points on the host and computes all their outputs."""
+    import torch
+
+    N, q = 4096, MED_Q
+    P = N * len(q)
+    shape = pirscan.RowselShape.make(N, q, D0, D1)
+    say(f"rowsel full size D0={D0} D1={D1} m={m}: synthesising {4 * P * D0 * D1 / 2**30:.1f} GiB")
+    d_db = empty_u32((D0, D1, P))
+    synth.fill_residues_(d_db, seed, synth.STREAM_ROWSEL_DB, N, q)
+    d_dbt = empty_u32((P, D0, D1))
+    pirscan.layout_db(shape, d_db, d_dbt)
+    del d_db
+    release()
+    outs = {}
+    for mm in m:
+        d_ct = empty_u32((mm, D0, P))
+        synth.fill_residues_(d_ct, seed, ct_stream, N, q)
+        d_out = empty_u32((mm, D1, P))
+        say(f"  scan m={mm}")
+        pirscan.rowsel_modgemm(shape, mm, d_ct, d_dbt, d_out)
+        pts = torch.tensor(points, device=d_out.device)
+        outs[mm] = to_host_u32(d_out.index_select(2, pts))
+        del d_ct, d_out
+    del d_dbt
+    release()
+    # host side: inputs of the sampled points only
+    pts = np.asarray(points, dtype=np.uint64)
+    qs = [q[int(p) // N] for p in points]
+    k = np.arange(D0, dtype=np.uint64)[:, None, None]
+    n = np.arange(D1, dtype=np.uint64)[None, :, None]
+    db_s = synth.residues(seed, synth.STREAM_ROWSEL_DB, (k * D1 + n) * P + pts[None, None, :], P, N, q)
+    for mm, got in outs.items():
+        mi = np.arange(mm, dtype=np.uint64)[:, None, None]
+        kk = np.arange(D0, dtype=np.uint64)[None, :, None]
+        ct_s = synth.residues(seed, ct_stream, (mi * D0 + kk) * P + pts[None, None, :], P, N, q)
+        want = oracle.rowsel(ct_s, db_s, 1, qs)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_medium_config_sampled():
+    pts = [0, 1, 63, 64, 4095, 4096, 6000, 8191, 8192, 12287]
+    sampled_full_size(3, 256, 256, [2], pts)
+
+
+def test_large_config_sampled():
+    """48 GiB DB, B=1 (m=2) and B=16 (m=32) sharing one tiled DB."""
+    pts = [0, 1, 2, 3, 4095, 4096, 4097, 9000, 12286, 12287]
+    sampled_full_size(4, 1024, 1024, [2, 32], pts)
