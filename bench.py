@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the PIR database-multiplication scan on one MI355X.
+
+One step = one pass of the whole scan path over both full-size databases:
+
+  * RowSel, 48 GiB NTT-domain DB (N=4096, R=3 primes of 29 bits, P=12288,
+    D0=D1=1024): a B=1 query (m=2) and a B=16 batch (m=32) sharing the tiled DB;
+  * scalar-HE, 64 GiB int8 DB (M=K=262144): a B=1 query and a B=32 batch.
+
+The tiled RowSel DB is built once by pirscan_layout_db before timing (the DB
+is static).  All inputs are seeded synthetic data resident in HBM before the
+timed region.  ``value`` = DB bytes scanned per step / step time (GB/s,
+1 GB = 1e9 B).  Per-scan times come from HIP events on the stream the kernels
+run on; the ``roofline`` object is for the scan that takes the most time.
+
+The ``cpu_baseline`` leg times the CPU oracle (oracle/, plain C) on a bounded
+sample of each of the four scans and reports the oracle's DB-scan rate for the
+same step mix.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (ops = 2 x MAC)
+# VALU 32x32->64-bit multiply-add (v_mad_u64_u32): 256 CUs x 4 SIMDs x 16
+# lanes per clock x 2.4 GHz = 39.3e12 MAC/s (half the issue rate of simple
+# 32-bit ops such as v_add_u32, which run 32 lanes per SIMD per clock).
+VALU_MAD64_PEAK_TMACS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+RS_N, RS_Q = 4096, [536813569, 536690689, 536641537]
+RS_D0 = RS_D1 = 1024
+SC_M = SC_K = 262144
+SEEDS = {"rowsel": 4, "scalar": 5}
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "rowsel": os.path.join(ROOT, "he_database_scan_amd", "csrc", "rowsel.hip"),
+    "scalar": os.path.join(ROOT, "he_database_scan_amd", "csrc", "scalar.hip"),
+}
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Workloads:
+    """Device-resident inputs and outputs of the four scans."""
+
+    def __init__(self):
+        import torch
+
+        import synth
+        from he_database_scan_amd import pirscan
+
+        self.torch, self.pirscan = torch, pirscan
+        dev = torch.device("cuda:0")
+        P = RS_N * len(RS_Q)
+        self.shape = pirscan.RowselShape.make(RS_N, RS_Q, RS_D0, RS_D1)
+        log("setup: RowSel 48 GiB DB (synthesise p-major, one-time relayout)")
+        db = torch.empty((RS_D0, RS_D1, P), dtype=torch.int32, device=dev)
+        synth.fill_residues_(db, SEEDS["rowsel"], synth.STREAM_ROWSEL_DB, RS_N, RS_Q)
+        self.dbt = torch.empty((P, RS_D0, RS_D1), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pirscan.layout_db(self.shape, db, self.dbt)
+        torch.cuda.synchronize()
+        self.layout_s = time.perf_counter() - t0
+        del db
+        torch.cuda.empty_cache()
+        self.ct, self.out = {}, {}
+        for m in (2, 32):
+            self.ct[m] = torch.empty((m, RS_D0, P), dtype=torch.int32, device=dev)
+            synth.fill_residues_(self.ct[m], SEEDS["rowsel"], synth.STREAM_ROWSEL_CT, RS_N, RS_Q)
+            self.out[m] = torch.empty((m, RS_D1, P), dtype=torch.int32, device=dev)
+        log("setup: scalar 64 GiB DB")
+        self.sdb = torch.empty((SC_M, SC_K), dtype=torch.int8, device=dev)
+        synth.fill_int8_(self.sdb, SEEDS["scalar"], synth.STREAM_SCALAR_DB)
+        self.q, self.sout, self.ws = {}, {}, {}
+        for B in (1, 32):
+            self.q[B] = torch.empty((SC_K, B), dtype=torch.int32, device=dev)
+            synth.fill_uint32_(self.q[B], SEEDS["scalar"], synth.STREAM_SCALAR_Q)
+            self.sout[B] = torch.empty((SC_M, B), dtype=torch.int32, device=dev)
+            self.ws[B] = torch.empty(pirscan.scalar_workspace_bytes(SC_M, SC_K, B), dtype=torch.uint8,
+                                     device=dev)
+        torch.cuda.synchronize()
+
+    # name -> (callable, DB bytes, algorithmic HBM bytes, queries, macs, kind)
+    def scans(self):
+        P = RS_N * len(RS_Q)
+        rs_db = 4 * P * RS_D0 * RS_D1
+        sc_db = SC_M * SC_K
+        pz = self.pirscan
+        out = {}
+        for m, B in ((2, 1), (32, 16)):
+            ct, o = self.ct[m], self.out[m]
+            out[f"rowsel_48GiB_B{B}"] = (
+                (lambda ct=ct, o=o, m=m: pz.rowsel_modgemm(self.shape, m, ct, self.dbt, o)),
+                rs_db, rs_db + 4 * P * m * (RS_D0 + RS_D1), B, P * m * RS_D0 * RS_D1, "rowsel")
+        for B in (1, 32):
+            q, o, ws = self.q[B], self.sout[B], self.ws[B]
+            out[f"scalar_64GiB_B{B}"] = (
+                (lambda q=q, o=o, ws=ws: pz.scalar_gemm_u32(self.sdb, q, o, ws)),
+                sc_db, sc_db + 4 * SC_K * B + 4 * SC_M * B, B, SC_M * SC_K * B, "scalar")
+        return out
+
+
+def roofline_for(name, ms, db_bytes, alg_bytes, macs):
+    if name == "rowsel_48GiB_B16":
+        achieved = macs / (ms * 1e-3) / 1e12
+        return {"bound": "alu", "achieved": achieved, "peak": VALU_MAD64_PEAK_TMACS, "unit": "TMAC/s",
+                "frac": achieved / VALU_MAD64_PEAK_TMACS}
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS}
+
+
+def traffic_for(name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (profiles/traffic.json), or None if absent or the kernel source changed."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(name)
+    if not ent:
+        return None
+    kind = "rowsel" if name.startswith("rowsel") else "scalar"
+    if ent.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s: float = 4.0):
+    """Times the oracle on bounded samples of the four scans (host cores) and
+    returns its DB-scan rate for the benchmark's step mix.  Each sample is
+    generated once (untimed) and the oracle's compute call is repeated until
+    about ``budget_s`` seconds have been spent on it."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = min(16, os.cpu_count() or 1)
+    P = RS_N * len(RS_Q)
+
+    def rowsel_sample(m, npts):
+        pts = np.linspace(0, P - 1, npts).astype(np.uint64)
+        k = np.arange(RS_D0, dtype=np.uint64)[:, None, None]
+        n = np.arange(RS_D1, dtype=np.uint64)[None, :, None]
+        db = synth.residues(SEEDS["rowsel"], synth.STREAM_ROWSEL_DB, (k * RS_D1 + n) * P + pts, P, RS_N, RS_Q)
+        mi = np.arange(m, dtype=np.uint64)[:, None, None]
+        kk = np.arange(RS_D0, dtype=np.uint64)[None, :, None]
+        ct = synth.residues(SEEDS["rowsel"], synth.STREAM_ROWSEL_CT, (mi * RS_D0 + kk) * P + pts, P, RS_N, RS_Q)
+        qs = [RS_Q[int(p) // RS_N] for p in pts]
+        return (lambda: oracle.rowsel(ct, db, 1, qs, nthreads=threads)), 4 * npts * RS_D0 * RS_D1, \
+            f"{npts} points x {RS_D0}x{RS_D1}, m={m}"
+
+    def scalar_sample(B, rows):
+        db = synth.int8_rows(SEEDS["scalar"], synth.STREAM_SCALAR_DB, SC_K, range(rows))
+        Q = synth.uint32_array(SEEDS["scalar"], synth.STREAM_SCALAR_Q, (SC_K, B))
+        return (lambda: oracle.scalar(db, Q, nthreads=threads)), rows * SC_K, f"{rows} rows x {SC_K}, B={B}"
+
+    rates, samples = {}, []
+    for name, make in (("rowsel_48GiB_B1", lambda: rowsel_sample(2, threads)),
+                       ("rowsel_48GiB_B16", lambda: rowsel_sample(32, threads)),
+                       ("scalar_64GiB_B1", lambda: scalar_sample(1, 4 * threads)),
+                       ("scalar_64GiB_B32", lambda: scalar_sample(32, threads))):
+        fn, nbytes, what = make()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                break
+        rates[name] = reps * nbytes / dt
+        samples.append(f"{name}: {what}, {reps} reps in {dt:.1f} s")
+    return rates, threads, "; ".join(samples)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="also run one torch copy of this many GiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the scan shards by points (RowSel) or DB rows (scalar-HE), see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = Workloads()
+    scans = w.scans()
+    stream = torch.cuda.current_stream()
+
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * 2**30)
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        for fn, *_ in scans.values():
+            fn()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    events = {name: [] for name in scans}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name, (fn, *_rest) in scans.items():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            events[name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {}
+    total_db = 0
+    for name, (fn, db_bytes, alg_bytes, queries, macs, kind) in scans.items():
+        ms_list = sorted(e0.elapsed_time(e1) for e0, e1 in events[name])
+        ms = sum(ms_list) / len(ms_list)
+        total_db += db_bytes
+        rf = roofline_for(name, ms, db_bytes, alg_bytes, macs)
+        rf["traffic"] = traffic_for(name)
+        per[name] = {"ms": ms, "ms_min": ms_list[0], "ms_median": ms_list[len(ms_list) // 2],
+                     "db_GBps": db_bytes / (ms * 1e-3) / 1e9, "qps": queries / (ms * 1e-3),
+                     "hbm_frac": db_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "roofline": rf}
+    ms_per_step = wall / args.steps * 1e3
+    value = total_db * args.steps / wall / 1e9
+    dominant = max(per, key=lambda k: per[k]["ms"])
+
+    result = {
+        "metric": "effective DB-scan GB/s and QPS at 48/64 GiB DB; % of HBM roofline",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32/s8 integer (exact)",
+        "data": "synthetic (seeded SplitMix64, generated on device)",
+        "config": {"workload": "rowsel-48GiB(B=1,B=16)+scalar-64GiB(B=1,B=32)",
+                   "rowsel": {"N": RS_N, "R": len(RS_Q), "q": RS_Q, "P": RS_N * len(RS_Q),
+                              "D0": RS_D0, "D1": RS_D1, "m": [2, 32]},
+                   "scalar": {"M": SC_M, "K": SC_K, "B": [1, 32]},
+                   "hbm_frac_of_step": value / HBM_PEAK_GBS,
+                   "layout_db_once_ms": w.layout_s * 1e3},
+        "roofline": dict(per[dominant]["roofline"], kernel=dominant),
+        "workloads": per,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on bounded samples)")
+        rates, cores, sample = cpu_baseline()
+        t_cpu = sum(scans[n][1] / rates[n] for n in scans)
+        result["cpu_baseline"] = {"value": total_db / t_cpu / 1e9, "unit": "GB/s", "cores": cores,
+                                  "kind": "oracle", "sample": sample,
+                                  "per_scan_GBps": {n: r / 1e9 for n, r in rates.items()}}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,13 +63,20 @@ __global__ __launch_bounds__(kThreads) void layout_db_kernel(const uint32_t* __r
 // ---------------------------------------------------------------------------
 // R2-R4: the scan.
 // ---------------------------------------------------------------------------
+// DB columns of one lane.  The DB is streamed exactly once per scan, so its
+// loads are non-temporal: they do not displace the staged ct lines and the
+// output lines that the workgroups on an XCD share in L2 (non-temporal 128-bit
+// reads also sustain a higher HBM read rate on gfx950 than cached ones).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int NPL>
 struct Vec;
 template <>
 struct Vec<4> {
   uint32_t v[4];
   __device__ __forceinline__ void load(const uint32_t* p) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
   }
 };
@@ -77,14 +84,14 @@ template <>
 struct Vec<2> {
   uint32_t v[2];
   __device__ __forceinline__ void load(const uint32_t* p) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
     v[0] = t.x; v[1] = t.y;
   }
 };
 template <>
 struct Vec<1> {
   uint32_t v[1];
-  __device__ __forceinline__ void load(const uint32_t* p) { v[0] = *p; }
+  __device__ __forceinline__ void load(const uint32_t* p) { v[0] = __builtin_nontemporal_load(p); }
 };
 
 // MR: ct rows handled per pass (m padded up to MR with zero rows).

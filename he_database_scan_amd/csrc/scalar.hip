@@ -39,6 +39,17 @@ constexpr uint64_t kMfmaKBlockMax = 16384;
 constexpr int kMfmaRowTiles = 4;                   // 4 x 16 rows per wavefront
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The DB is streamed once per scan: non-temporal 128-bit loads (they keep the
+// query digits resident in L2 and sustain a higher HBM read rate).
+__device__ __forceinline__ uint4 load_db16(const int8_t* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ v4i load_db16_v4i(const int8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
 
 __device__ __forceinline__ uint32_t signed_digits_word(uint32_t w) {
   return (w + 0x80808080u) ^ 0x80808080u;
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const int8_t* __restrict
 #pragma unroll
       for (int t = 0; t < kGemvJ; ++t) {
         v[rr][t] = (row_on && chunk_on[t])
-                       ? *reinterpret_cast<const uint4*>(base + (r + rr) * K + t * 1024)
+                       ? load_db16(base + (r + rr) * K + t * 1024)
                        : make_uint4(0, 0, 0, 0);
       }
     }
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const int8_t* __restrict
     v4i a[kMfmaRowTiles];
 #pragma unroll
     for (int rt = 0; rt < kMfmaRowTiles; ++rt)
-      a[rt] = (row_on[rt] && k_on) ? *reinterpret_cast<const v4i*>(arow[rt] + kc) : v4i{0, 0, 0, 0};
+      a[rt] = (row_on[rt] && k_on) ? load_db16_v4i(arow[rt] + kc) : v4i{0, 0, 0, 0};
     const v4i* bsrc = reinterpret_cast<const v4i*>(dig) + (kc / 16) * dcols + li;
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
