@@ -36,19 +36,21 @@ constexpr uint64_t kGemvKBlock = 64 * 16 * kGemvJ;  // 4096
 constexpr int kGemvRowsPerWave = 64;
 constexpr int kGemvRowBatch = 4;
 constexpr uint64_t kMfmaKBlockMax = 16384;
-constexpr int kMfmaRowTiles = 4;                   // 4 x 16 rows per wavefront
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The DB is streamed once per scan: non-temporal 128-bit loads (they keep the
-// query digits resident in L2 and sustain a higher HBM read rate).
+// The GEMV streams each DB row segment once with non-temporal 128-bit loads
+// (measured faster than cached loads for pure streaming on gfx950).  The MFMA
+// kernel reads every 128-byte row line as two 64-byte halves issued back to
+// back; plain cached loads let the second half hit the line the first one
+// brought in (measured faster than non-temporal loads there).
 __device__ __forceinline__ uint4 load_db16(const int8_t* p) {
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 __device__ __forceinline__ v4i load_db16_v4i(const int8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+  return *reinterpret_cast<const v4i*>(p);
 }
 
 __device__ __forceinline__ uint32_t signed_digits_word(uint32_t w) {
@@ -203,61 +205,166 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const uint32_t* __
 }
 
 // ---------------------------------------------------------------------------
-// S3: int8 MFMA GEMM.  Workgroup = 4 wavefronts x 64 rows of one k-block.
-// NT = 16-column tiles = 4 * bpad / 16.
+// S3: int8 MFMA GEMM.  A tile = 8 wavefronts x kMfmaRowTiles2*16 rows of one
+// k-block; NT = 16-column tiles = 4 * bpad / 16.  The kernel is persistent:
+// one workgroup per CU walks a list of tiles.  The tiles are split into 8
+// contiguous ranges, one per XCD, and the workgroups of an XCD take the tiles
+// of its range round-robin, so they start together on the same k-block and
+// read the same digit chunks at nearly the same time: each chunk is fetched
+// into that XCD's L2 once and reused by all its workgroups.
+//  * Digit fragments (the B operand, shared by all rows) are staged once per
+//    workgroup into LDS in chunks of 256 k, double-buffered: the next chunk is
+//    loaded into registers at the start of a chunk and written to LDS at its
+//    end, one barrier per chunk.
+//  * DB rows (the A operand, each byte used by exactly one wavefront) stream
+//    straight into registers through a ring of kMfmaDepth 64-k steps: the
+//    slot consumed by a step is refilled with the step kMfmaDepth ahead, so
+//    ~kMfmaDepth * 2 KiB per wavefront are in flight without extra registers.
 // ---------------------------------------------------------------------------
-template <int NT>
-__global__ __launch_bounds__(kThreads) void mfma_kernel(const int8_t* __restrict__ db,
-                                                        const uint8_t* __restrict__ dig,
-                                                        uint32_t* __restrict__ dst, uint64_t M,
-                                                        uint64_t K, uint64_t kblock, uint64_t nkb,
-                                                        uint64_t row_blocks, uint32_t bgroup,
-                                                        uint64_t ldd, uint32_t dcol0) {
-  constexpr int HT = NT / 4;  // column tiles per digit plane
-  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
-  const uint64_t kb = wg / row_blocks, rb = wg % row_blocks;
-  const uint64_t row0 = (rb * (kThreads / 64) + wave) * (16 * kMfmaRowTiles);
-  if (row0 >= M) return;  // no barriers below
-  const uint32_t li = lane % 16, lg = lane / 16;
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaRowTiles2 = 2;                  // 2 x 16 rows per wavefront
+constexpr int kMfmaDepth = 8;                      // A ring depth in 64-k steps
+static_assert(kMfmaDepth % 4 == 0, "the ring turns in whole B chunks");
+constexpr int kMfmaChunkSteps = 4;                 // B chunk = 4 steps = 256 k
+constexpr uint64_t kMfmaChunkK = 64 * kMfmaChunkSteps;
 
-  v4i acc[kMfmaRowTiles][NT];
+template <int NT>
+struct MfmaShape {
+  static constexpr int HT = NT / 4;                        // column tiles per digit plane
+  static constexpr int DCOLS = 16 * NT;                    // 4 * bpad digit columns
+  static constexpr int CHUNK_BYTES = kMfmaChunkK * DCOLS;  // 32 KiB at bpad = 32
+  static constexpr int PIECES = CHUNK_BYTES / 16 / (64 * kMfmaWaves);  // 16-byte pieces per thread
+  static_assert(PIECES >= 1 && CHUNK_BYTES % (16 * 64 * kMfmaWaves) == 0, "chunk tiling");
+};
+
+// One tile (kb, rb).  Starts and ends with every wave past a barrier, so the
+// LDS buffers are free on entry and on exit.
+template <int NT>
+__device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const uint8_t* dig,
+                                          uint32_t* __restrict__ dst, uint64_t M, uint64_t K,
+                                          uint64_t kblock, uint64_t nkb, uint32_t bgroup, uint64_t ldd,
+                                          uint32_t dcol0, uint64_t kb, uint64_t rb,
+                                          uint8_t (*bsm)[MfmaShape<NT>::CHUNK_BYTES]) {
+  constexpr int HT = MfmaShape<NT>::HT;
+  constexpr int DCOLS = MfmaShape<NT>::DCOLS;
+  constexpr int CHUNK_BYTES = MfmaShape<NT>::CHUNK_BYTES;
+  constexpr int PIECES = MfmaShape<NT>::PIECES;
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t row0 = (rb * kMfmaWaves + wave) * (16 * kMfmaRowTiles2);
+  const uint32_t li = lane % 16, lg = lane / 16;
+  const uint64_t kbeg = kb * kblock;
+  const uint32_t nsteps = (uint32_t)(kblock / 64);
+  const uint32_t nchunks = nsteps / kMfmaChunkSteps;
+
+  // A rows past M and k past K are read from clamped (valid) addresses: rows
+  // past M are never stored, and k past K meets zero digits.
+  const int8_t* arow[kMfmaRowTiles2];
 #pragma unroll
-  for (int rt = 0; rt < kMfmaRowTiles; ++rt)
+  for (int rt = 0; rt < kMfmaRowTiles2; ++rt) {
+    const uint64_t row = row0 + rt * 16 + li;
+    arow[rt] = db + (row < M ? row : M - 1) * K;
+  }
+  const uint64_t klast = K - 16;  // last valid 16-byte chunk of a row (K % 16 == 0)
+
+  // chunk c of this k-block is CHUNK_BYTES contiguous bytes of the digit array
+  // (dig is not __restrict__: the compiler barrier below must be able to
+  // order these loads, which restrict would let the compiler ignore.)
+  const u32x4* bsrc = reinterpret_cast<const u32x4*>(dig + (kbeg / 16) * (uint64_t)DCOLS * 16) + tid;
+  u32x4* bdst0 = reinterpret_cast<u32x4*>(bsm[0]) + tid;
+  u32x4* bdst1 = reinterpret_cast<u32x4*>(bsm[1]) + tid;
+
+  v4i acc[kMfmaRowTiles2][NT];
+#pragma unroll
+  for (int rt = 0; rt < kMfmaRowTiles2; ++rt)
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) acc[rt][ct] = v4i{0, 0, 0, 0};
 
-  bool row_on[kMfmaRowTiles];
-  const int8_t* arow[kMfmaRowTiles];
+  // prologue: A ring for steps 0..depth-1, B chunk 0 into LDS
+  v4i a[kMfmaDepth][kMfmaRowTiles2];
 #pragma unroll
-  for (int rt = 0; rt < kMfmaRowTiles; ++rt) {
-    const uint64_t row = row0 + rt * 16 + li;
-    row_on[rt] = row < M;
-    arow[rt] = db + (row_on[rt] ? row : 0) * K;
+  for (int d = 0; d < kMfmaDepth; ++d) {
+    uint64_t ko = kbeg + (uint64_t)d * 64 + 16 * lg;
+    ko = ko < klast ? ko : klast;
+#pragma unroll
+    for (int rt = 0; rt < kMfmaRowTiles2; ++rt) a[d][rt] = load_db16_v4i(arow[rt] + ko);
   }
-  const uint64_t kbeg = kb * kblock;
-  const uint64_t kend = kbeg + kblock;  // digits are zero-padded up to nkb*kblock
-  const uint32_t dcols = 4 * NT * 4;    // 4 * bpad digit columns
-  for (uint64_t kk = kbeg; kk < kend; kk += 64) {
-    const uint64_t kc = kk + 16 * lg;
-    const bool k_on = kc < K;
-    v4i a[kMfmaRowTiles];
+  {
+    u32x4 breg[PIECES];
 #pragma unroll
-    for (int rt = 0; rt < kMfmaRowTiles; ++rt)
-      a[rt] = (row_on[rt] && k_on) ? load_db16_v4i(arow[rt] + kc) : v4i{0, 0, 0, 0};
-    const v4i* bsrc = reinterpret_cast<const v4i*>(dig) + (kc / 16) * dcols + li;
+    for (int i = 0; i < PIECES; ++i) breg[i] = bsrc[i * (64 * kMfmaWaves)];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const v4i bf = bsrc[ct * 16];
+    for (int i = 0; i < PIECES; ++i) bdst0[i * (64 * kMfmaWaves)] = breg[i];
+  }
+  __syncthreads();
+
+  constexpr int kChunksPerTurn = kMfmaDepth / kMfmaChunkSteps;  // one turn of the A ring
+  for (uint32_t c = 0; c < nchunks; c += kChunksPerTurn) {
+    // a whole ring turn per iteration so that every ring slot index is static
 #pragma unroll
-      for (int rt = 0; rt < kMfmaRowTiles; ++rt)
-        acc[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[rt], bf, acc[rt][ct], 0, 0, 0);
+    for (int half = 0; half < kChunksPerTurn; ++half) {
+      const uint32_t cc = c + half;
+      if (cc < nchunks) {
+        // next chunk (or this one again at the end: same bytes, harmless)
+        const uint32_t cn = cc + 1 < nchunks ? cc + 1 : cc;
+        u32x4 breg[PIECES];
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i)
+          breg[i] = bsrc[(uint64_t)cn * (CHUNK_BYTES / 16) + i * (64 * kMfmaWaves)];
+        // Issue the chunk loads here, a whole chunk before their LDS store:
+        // the empty asm is a compiler memory barrier that stops the loads from
+        // being merged with that store (into a copy at the end of the chunk),
+        // and the scheduling barrier stops the scheduler from sinking them.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const v4i* bl = reinterpret_cast<const v4i*>(bsm[cc & 1]);
+#pragma unroll
+        for (int s = 0; s < kMfmaChunkSteps; ++s) {
+          const uint32_t step = cc * kMfmaChunkSteps + s;
+          const int slot = (half * kMfmaChunkSteps + s) % kMfmaDepth;
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const v4i bf = bl[(s * 4 + lg) * DCOLS + ct * 16 + li];
+#pragma unroll
+            for (int rt = 0; rt < kMfmaRowTiles2; ++rt)
+              acc[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[slot][rt], bf, acc[rt][ct], 0, 0, 0);
+          }
+          if (s & 1) {
+            // Refill the slots of steps s-1 and s together: the two 64-byte
+            // halves of each 128-byte row line are requested back to back, so
+            // the line is fetched from HBM once.  Past the last step the
+            // refill re-reads the last step (valid, unused): keeping it
+            // unconditional keeps the chunk one basic block, so the compiler
+            // cannot sink the digit-chunk loads down to their LDS store.
+            uint32_t nxt = step - 1 + kMfmaDepth;
+            nxt = nxt < nsteps ? nxt : nsteps - 2;
+            uint64_t ko0 = kbeg + (uint64_t)nxt * 64 + 16 * lg;
+            uint64_t ko1 = ko0 + 64;
+            ko0 = ko0 < klast ? ko0 : klast;
+            ko1 = ko1 < klast ? ko1 : klast;
+#pragma unroll
+            for (int rt = 0; rt < kMfmaRowTiles2; ++rt) {
+              a[slot - 1][rt] = load_db16_v4i(arow[rt] + ko0);
+              a[slot][rt] = load_db16_v4i(arow[rt] + ko1);
+            }
+            // keep the refill here: the scheduler would otherwise sink it
+            // next to its use (to save registers) and undo the prefetch
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // The other buffer was last read in chunk cc-1, which every wave
+        // finished before the previous barrier.
+        u32x4* bdst = (cc & 1) ? bdst0 : bdst1;
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) bdst[i * (64 * kMfmaWaves)] = breg[i];
+        __syncthreads();
+      }
     }
   }
 
   // D element i of lane l is (row 4*(l/16) + i, column l%16) of the tile.
 #pragma unroll
-  for (int rt = 0; rt < kMfmaRowTiles; ++rt) {
+  for (int rt = 0; rt < kMfmaRowTiles2; ++rt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t row = row0 + rt * 16 + 4 * lg + i;
@@ -274,6 +381,24 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const int8_t* __restrict
       }
     }
   }
+}
+
+template <int NT>
+__global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(const int8_t* __restrict__ db,
+                                                               const uint8_t* dig,
+                                                               uint32_t* __restrict__ dst, uint64_t M,
+                                                               uint64_t K, uint64_t kblock, uint64_t nkb,
+                                                               uint64_t row_blocks, uint32_t bgroup,
+                                                               uint64_t ldd, uint32_t dcol0) {
+  __shared__ __attribute__((aligned(16))) uint8_t bsm[2][MfmaShape<NT>::CHUNK_BYTES];
+  constexpr uint32_t kXcds = 8;
+  const uint32_t hw = blockIdx.x, G = gridDim.x;  // G >= kXcds (host guarantees)
+  const uint32_t xcd = hw % kXcds, j = hw / kXcds;
+  const uint32_t per_xcd = (G - xcd + kXcds - 1) / kXcds;  // workgroups with this residue
+  const uint64_t tiles = nkb * row_blocks;
+  const uint64_t lo = tiles * xcd / kXcds, hi = tiles * (xcd + 1) / kXcds;
+  for (uint64_t t = lo + j; t < hi; t += per_xcd)
+    mfma_tile<NT>(db, dig, dst, M, K, kblock, nkb, bgroup, ldd, dcol0, t / row_blocks, t % row_blocks, bsm);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,12 +450,21 @@ template <int NT>
 hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint64_t M, uint64_t K,
                        const ScalarPlan& pl, uint32_t bgroup, uint64_t ldd, uint32_t dcol0,
                        hipStream_t stream) {
-  const uint64_t rows_per_wg = (kThreads / 64) * 16 * kMfmaRowTiles;
+  const uint64_t rows_per_wg = kMfmaWaves * 16 * kMfmaRowTiles2;
   const uint64_t row_blocks = ceil_div(M, rows_per_wg);
-  const uint64_t grid = row_blocks * pl.nkb;
-  if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_kernel<NT>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, db, dig, dst,
-                     M, K, pl.kblock, pl.nkb, row_blocks, bgroup, ldd, dcol0);
+  if (pl.kblock % kMfmaChunkK != 0) return hipErrorInvalidValue;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<NT>, 64 * kMfmaWaves, 0);
+  if (e != hipSuccess) return e;
+  // persistent: as many workgroups as are co-resident, at least one per XCD
+  uint64_t grid = (uint64_t)cus * (uint64_t)(per_cu > 0 ? per_cu : 1);
+  if (grid > row_blocks * pl.nkb) grid = row_blocks * pl.nkb;
+  if (grid < 8) grid = 8;
+  hipLaunchKernelGGL((mfma_kernel<NT>), dim3((uint32_t)grid), dim3(64 * kMfmaWaves), 0, stream, db, dig,
+                     dst, M, K, pl.kblock, pl.nkb, row_blocks, bgroup, ldd, dcol0);
   return hipGetLastError();
 }
 
@@ -359,7 +493,7 @@ bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPl
     p->mfma = true;
     p->bgroup = B < 32 ? B : 32;
     p->bpad = (uint32_t)align_up(p->bgroup, 16);
-    p->kblock = K > kMfmaKBlockMax ? kMfmaKBlockMax : align_up(K, 64);
+    p->kblock = K > kMfmaKBlockMax ? kMfmaKBlockMax : align_up(K, kMfmaChunkK);
     p->nkb = ceil_div(K, p->kblock);
     p->kpad = p->nkb * p->kblock;
     p->digit_bytes = p->kpad * 4 * p->bpad;
