@@ -68,42 +68,70 @@ __global__ __launch_bounds__(kThreads) void layout_db_kernel(const uint32_t* __r
 // output lines that the workgroups on an XCD share in L2 (non-temporal 128-bit
 // reads also sustain a higher HBM read rate on gfx950 than cached ones).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int NPL>
+// NT: non-temporal loads, used when each DB word is loaded by exactly one
+// lane.  With several row groups per wavefront (G > 1) the same words are
+// loaded by G lanes of one instruction, and only cached loads let the later
+// lanes hit the line the first one brought in (non-temporal ones re-fetch it
+// from HBM).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld4(const uint32_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t ld1(const uint32_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int NPL, bool NT>
 struct Vec;
-template <>
-struct Vec<4> {
+template <bool NT>
+struct Vec<8, NT> {
+  uint32_t v[8];
+  __device__ __forceinline__ void load(const uint32_t* p) {
+    const u32x4 t0 = ld4<NT>(p), t1 = ld4<NT>(p + 4);
+    v[0] = t0.x; v[1] = t0.y; v[2] = t0.z; v[3] = t0.w;
+    v[4] = t1.x; v[5] = t1.y; v[6] = t1.z; v[7] = t1.w;
+  }
+};
+template <bool NT>
+struct Vec<4, NT> {
   uint32_t v[4];
   __device__ __forceinline__ void load(const uint32_t* p) {
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 t = ld4<NT>(p);
     v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
   }
 };
-template <>
-struct Vec<2> {
-  uint32_t v[2];
-  __device__ __forceinline__ void load(const uint32_t* p) {
-    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-    v[0] = t.x; v[1] = t.y;
-  }
-};
-template <>
-struct Vec<1> {
+template <bool NT>
+struct Vec<1, NT> {
   uint32_t v[1];
-  __device__ __forceinline__ void load(const uint32_t* p) { v[0] = __builtin_nontemporal_load(p); }
+  __device__ __forceinline__ void load(const uint32_t* p) { v[0] = ld1<NT>(p); }
 };
 
-// MR: ct rows handled per pass (m padded up to MR with zero rows).
-// NPL: DB columns per lane (128/64/32-bit loads).
+// MR:  ct rows handled per pass (m padded up to MR with zero rows).
+// G:   row groups per wavefront.  Lane l works on rows [g*MR/G, (g+1)*MR/G)
+//      of the pass, g = l / (64/G), and on NPL columns; so each ct value read
+//      from LDS feeds NPL products and each DB word feeds MR/G products.  With
+//      G = 1 the ct values are wave-uniform LDS broadcasts; for large MR,
+//      G > 1 cuts the LDS traffic per product by G at the same product count
+//      per wavefront (LDS bandwidth, not the multiplier, would otherwise bound
+//      the scan).
+// NPL: DB columns per lane (256/128/32-bit loads).
 // UNR: k-rows whose loads are issued back to back (must divide the fold).
-template <int MR, int NPL, int UNR>
+template <int MR, int G, int NPL, int UNR>
 __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32_t m_base,
                                                           uint32_t nslices, uint64_t items) {
   constexpr int KC = kLdsWords / (kWaves * MR);  // k-rows per staged chunk
+  constexpr int RPL = MR / G;                    // rows per lane
+  constexpr int LPG = 64 / G;                    // lanes per row group
+  constexpr bool NT = G == 1;
+  static_assert(MR % G == 0 && 64 % G == 0 && (RPL == 1 || RPL % 2 == 0), "row split");
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];  // [point][KC][MR]
 
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t grp = lane / LPG, col = lane % LPG;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const uint64_t item0 = (uint64_t)wg * kWaves;
   const uint64_t item_last = (item0 + kWaves < items ? item0 + kWaves : items) - 1;
@@ -114,15 +142,15 @@ __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32
   const uint64_t p = wave_on ? item / nslices : p_lo;
   const uint32_t pl = (uint32_t)(p - p_lo);
   const uint32_t slice = wave_on ? (uint32_t)(item % nslices) : 0u;
-  const uint32_t n0 = (slice * 64u + lane) * NPL;
+  const uint32_t n0 = (slice * LPG + col) * NPL;
   const bool lane_on = wave_on && n0 < a.D1;
   const uint32_t limb = (uint32_t)(p / a.N);
   const uint64_t cfold = a.lc.c[limb];
   const uint32_t mrows = (a.m - m_base) < (uint32_t)MR ? (a.m - m_base) : (uint32_t)MR;
 
-  uint64_t acc[MR][NPL];
+  uint64_t acc[RPL][NPL];
 #pragma unroll
-  for (int i = 0; i < MR; ++i)
+  for (int i = 0; i < RPL; ++i)
 #pragma unroll
     for (int j = 0; j < NPL; ++j) acc[i][j] = 0;
 
@@ -143,40 +171,42 @@ __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32
     }
     __syncthreads();
     if (lane_on) {
-      const uint32_t* L = lds + pl * (KC * MR);
+      const uint32_t* L = lds + pl * (KC * MR) + grp * RPL;
       for (uint32_t s0 = 0; s0 < kc; s0 += a.fold) {
         const uint32_t s1 = (s0 + a.fold < kc) ? s0 + a.fold : kc;
         uint32_t kk = s0;
         if constexpr (UNR > 1) {
           for (; kk + UNR <= s1; kk += UNR) {
-            Vec<NPL> d[UNR];
+            Vec<NPL, NT> d[UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) d[u].load(dbp + (uint64_t)(k0 + kk + u) * a.D1);
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-              uint32_t cv[MR];
-              if constexpr (MR == 2) {
+              uint32_t cv[RPL];
+              if constexpr (RPL == 1) {
+                cv[0] = L[(kk + u) * MR];
+              } else if constexpr (RPL == 2) {
                 const uint2 t = *reinterpret_cast<const uint2*>(L + (kk + u) * MR);
                 cv[0] = t.x; cv[1] = t.y;
               } else {
 #pragma unroll
-                for (int i = 0; i < MR; i += 4) {
+                for (int i = 0; i < RPL; i += 4) {
                   const uint4 t = *reinterpret_cast<const uint4*>(L + (kk + u) * MR + i);
                   cv[i] = t.x; cv[i + 1] = t.y; cv[i + 2] = t.z; cv[i + 3] = t.w;
                 }
               }
 #pragma unroll
-              for (int i = 0; i < MR; ++i)
+              for (int i = 0; i < RPL; ++i)
 #pragma unroll
                 for (int j = 0; j < NPL; ++j) acc[i][j] += (uint64_t)cv[i] * d[u].v[j];
             }
           }
         }
         for (; kk < s1; ++kk) {
-          Vec<NPL> d;
+          Vec<NPL, NT> d;
           d.load(dbp + (uint64_t)(k0 + kk) * a.D1);
 #pragma unroll
-          for (int i = 0; i < MR; ++i) {
+          for (int i = 0; i < RPL; ++i) {
             const uint64_t cvi = L[kk * MR + i];
 #pragma unroll
             for (int j = 0; j < NPL; ++j) acc[i][j] += cvi * d.v[j];
@@ -184,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32
         }
         // fold: hi*2^32 + lo == hi*(2^32 mod q) + lo  (mod q)
 #pragma unroll
-        for (int i = 0; i < MR; ++i)
+        for (int i = 0; i < RPL; ++i)
 #pragma unroll
           for (int j = 0; j < NPL; ++j)
             acc[i][j] = (acc[i][j] >> 32) * cfold + (uint32_t)acc[i][j];
@@ -196,43 +226,44 @@ __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32
     const uint64_t q = a.lc.q[limb];
     const uint64_t mu = a.lc.mu[limb];
 #pragma unroll
-    for (int i = 0; i < MR; ++i) {
-      if ((uint32_t)i < mrows) {
+    for (int i = 0; i < RPL; ++i) {
+      const uint32_t mi = grp * RPL + i;
+      if (mi < mrows) {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
           // Barrett with mu = floor((2^64-1)/q): the estimate is at most one short.
           const uint64_t x = acc[i][j];
           uint64_t r = x - __umul64hi(x, mu) * q;
           if (r >= q) r -= q;
-          a.out[((uint64_t)(m_base + i) * a.D1 + n0 + j) * a.P + p] = (uint32_t)r;
+          a.out[((uint64_t)(m_base + mi) * a.D1 + n0 + j) * a.P + p] = (uint32_t)r;
         }
       }
     }
   }
 }
 
-template <int MR, int NPL, int UNR>
+template <int MR, int G, int NPL, int UNR>
 hipError_t launch_one(const RowselLaunch& a, uint32_t m_base, hipStream_t stream) {
-  const uint32_t cols_per_wave = 64u * NPL;
+  const uint32_t cols_per_wave = (64u / G) * NPL;
   const uint32_t nslices = (a.D1 + cols_per_wave - 1) / cols_per_wave;
   const uint64_t items = a.P * nslices;
   const uint64_t grid = (items + kWaves - 1) / kWaves;
   if (grid == 0 || grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((rowsel_kernel<MR, NPL, UNR>), dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((rowsel_kernel<MR, G, NPL, UNR>), dim3((uint32_t)grid), dim3(kThreads), 0, stream,
                      a, m_base, nslices, items);
   return hipGetLastError();
 }
 
 // Picks the widest column vector the shape allows, then the unroll the fold
 // period allows.
-template <int MR, int NPL_MAX>
+template <int MR, int G, int NPL_MAX>
 hipError_t launch_mr(const RowselLaunch& a, uint32_t m_base, hipStream_t stream) {
-  constexpr int U = MR <= 8 ? 8 : 4;
+  constexpr int U = (MR / G) * NPL_MAX <= 16 ? 8 : 4;
   const bool wide = (a.D1 % NPL_MAX) == 0 &&
-                    (reinterpret_cast<uintptr_t>(a.dbt) % (4u * NPL_MAX)) == 0;
-  if ((a.fold % U) != 0) return launch_one<MR, 1, 1>(a, m_base, stream);
-  if (wide) return launch_one<MR, NPL_MAX, U>(a, m_base, stream);
-  return launch_one<MR, 1, U>(a, m_base, stream);
+                    (reinterpret_cast<uintptr_t>(a.dbt) % (4u * (NPL_MAX > 4 ? 4 : NPL_MAX))) == 0;
+  if ((a.fold % U) != 0) return launch_one<MR, G, 1, 1>(a, m_base, stream);
+  if (wide) return launch_one<MR, G, NPL_MAX, U>(a, m_base, stream);
+  return launch_one<MR, G, 1, U>(a, m_base, stream);
 }
 
 }  // namespace
@@ -270,11 +301,11 @@ hipError_t launch_rowsel(const RowselLaunch& a, hipStream_t stream) {
   for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
     const uint32_t rows = a.m - m_base;
     hipError_t e;
-    if (rows <= 2) e = launch_mr<2, 4>(a, m_base, stream);
-    else if (rows <= 4) e = launch_mr<4, 4>(a, m_base, stream);
-    else if (rows <= 8) e = launch_mr<8, 4>(a, m_base, stream);
-    else if (rows <= 16) e = launch_mr<16, 2>(a, m_base, stream);
-    else e = launch_mr<32, 2>(a, m_base, stream);
+    if (rows <= 2) e = launch_mr<2, 1, 4>(a, m_base, stream);
+    else if (rows <= 4) e = launch_mr<4, 1, 4>(a, m_base, stream);
+    else if (rows <= 8) e = launch_mr<8, 2, 4>(a, m_base, stream);
+    else if (rows <= 16) e = launch_mr<16, 2, 8>(a, m_base, stream);
+    else e = launch_mr<32, 2, 4>(a, m_base, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
