@@ -145,6 +145,61 @@ def traffic_for(name):
     return ent.get("bytes_per_launch")
 
 
+# The kernel that dominates each scan (the one the roofline and traffic refer to).
+SCAN_KERNELS = {
+    "rowsel_48GiB_B1": "rowsel_kernel<2,",
+    "rowsel_48GiB_B16": "rowsel_kernel<32,",
+    "scalar_64GiB_B1": "gemv_kernel",
+    "scalar_64GiB_B32": "mfma_kernel<8>",
+}
+
+
+def _short_kernel_name(name: str) -> str:
+    for pre in ("void ", "pirscan::(anonymous namespace)::", "(anonymous namespace)::"):
+        name = name.replace(pre, "")
+    return name.split("(")[0]
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, calib_gib: float) -> dict:
+    """Turns two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
+    WRITE_SIZE, both with --calib-copy-gib) into HBM bytes per launch of each
+    scan's dominant kernel.  Each counter is scaled by what it reads for the
+    plain copy of calib_gib GiB (the largest copy kernel in the run)."""
+    import csv
+    import statistics
+
+    def load(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(_short_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"calibration": {}}
+    per = {}
+    for kind, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        vals = load(path, counter)
+        copies = [v for k, vs in vals.items() if "copy" in k.lower() for v in vs]
+        if not copies:
+            raise SystemExit(f"no copy kernel in {path}: run the profile with --calib-copy-gib")
+        scale = calib_gib * 2**30 / (max(copies) * 1024.0)  # true bytes per counted byte
+        out["calibration"][counter] = {"copy_bytes": calib_gib * 2**30, "counter_KiB": max(copies),
+                                       "scale": scale}
+        for scan, pat in SCAN_KERNELS.items():
+            hits = [v for k, vs in vals.items() if k.startswith(pat) for v in vs]
+            if hits:
+                per.setdefault(scan, {})[kind + "_bytes"] = statistics.median(hits) * 1024.0 * scale
+                per[scan]["kernel"] = [k for k in vals if k.startswith(pat)][0]
+    for scan, ent in per.items():
+        if "fetch_bytes" in ent and "write_bytes" in ent:
+            ent["bytes_per_launch"] = ent["fetch_bytes"] + ent["write_bytes"]
+            kind = "rowsel" if scan.startswith("rowsel") else "scalar"
+            ent["source_sha256_16"] = source_hash(KERNEL_SOURCES[kind])
+            out[scan] = ent
+    return out
+
+
 def cpu_baseline(budget_s: float = 4.0):
     """Times the oracle on bounded samples of the four scans (host cores) and
     returns its DB-scan rate for the benchmark's step mix.  Each sample is
@@ -201,7 +256,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one torch copy of this many GiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc counter "
+                         "collections (FETCH_SIZE, WRITE_SIZE) of this benchmark")
     args = ap.parse_args()
+    if args.traffic_from:
+        res = traffic_from_counters(*args.traffic_from, calib_gib=args.calib_copy_gib or 4.0)
+        json.dump(res, open(TRAFFIC_FILE, "w"), indent=1)
+        print(json.dumps(res, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the scan shards by points (RowSel) or DB rows (scalar-HE), see DESIGN.md", file=sys.stderr)
