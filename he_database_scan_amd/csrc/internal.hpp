@@ -31,8 +31,15 @@ struct RowselLaunch {
 hipError_t launch_layout_db(const uint32_t* src, uint32_t* dst, uint64_t X, uint64_t P,
                             hipStream_t stream);
 
-// R2-R4: the modular GEMM scan.
+// R2-R4: the modular GEMM scan on the VALU (any m, any q < 2^32).
 hipError_t launch_rowsel(const RowselLaunch& a, hipStream_t stream);
+
+// Batched RowSel on int8 MFMA: m >= kRowselMfmaMinRows, every q < 2^31,
+// D0 <= 16384.  Needs a workspace of rowsel_mfma_workspace_bytes().
+constexpr uint32_t kRowselMfmaMinRows = 16;
+bool rowsel_mfma_eligible(const RowselLaunch& a, uint32_t R);
+size_t rowsel_mfma_workspace_bytes(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1);
+hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace, hipStream_t stream);
 
 // Products of (q-1)^2 that fit between folds for modulus q (host helper).
 uint32_t rowsel_fold_period(uint32_t q);

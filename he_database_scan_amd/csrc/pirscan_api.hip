@@ -85,39 +85,69 @@ int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor, 
                                                  (hipStream_t)stream));
 }
 
-int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint32_t* ct,
-                           const uint32_t* db_tiled, uint32_t* out, void* stream) {
-  uint64_t P = 0, words = 0;
-  if (!rowsel_shape_ok(s, &P, &words) || m == 0 || !ct || !db_tiled || !out) return PIRSCAN_EINVAL;
-  const unsigned __int128 ct_words = (unsigned __int128)m * s->D0 * P;
-  const unsigned __int128 out_words = (unsigned __int128)m * s->D1 * P;
-  if (ct_words * 4 > (unsigned __int128)(~(uint64_t)0 >> 1) ||
-      out_words * 4 > (unsigned __int128)(~(uint64_t)0 >> 1))
-    return PIRSCAN_EINVAL;
-  if (overlap(out, (uint64_t)out_words * 4, ct, (uint64_t)ct_words * 4) ||
-      overlap(out, (uint64_t)out_words * 4, db_tiled, words * 4))
-    return PIRSCAN_EINVAL;
-  const int dc = device_check();
-  if (dc != PIRSCAN_OK) return dc;
-
-  pirscan::RowselLaunch a{};
-  a.ct = ct;
-  a.dbt = db_tiled;
-  a.out = out;
-  a.P = P;
-  a.N = s->N;
-  a.D0 = s->D0;
-  a.D1 = s->D1;
-  a.m = m;
-  a.fold = 32;
+// Fills the launch description (pointers may be null when only sizes are
+// wanted).  Returns false on an invalid shape or m.
+static bool rowsel_launch_desc(const pirscan_rowsel_shape* s, uint32_t m, const uint32_t* ct,
+                               const uint32_t* db_tiled, uint32_t* out, pirscan::RowselLaunch* a,
+                               uint64_t* db_words, uint64_t* ct_words, uint64_t* out_words) {
+  uint64_t P = 0;
+  if (!rowsel_shape_ok(s, &P, db_words) || m == 0) return false;
+  const unsigned __int128 cw = (unsigned __int128)m * s->D0 * P;
+  const unsigned __int128 ow = (unsigned __int128)m * s->D1 * P;
+  if (cw * 4 > (unsigned __int128)(~(uint64_t)0 >> 1) || ow * 4 > (unsigned __int128)(~(uint64_t)0 >> 1))
+    return false;
+  *ct_words = (uint64_t)cw;
+  *out_words = (uint64_t)ow;
+  *a = pirscan::RowselLaunch{};
+  a->ct = ct;
+  a->dbt = db_tiled;
+  a->out = out;
+  a->P = P;
+  a->N = s->N;
+  a->D0 = s->D0;
+  a->D1 = s->D1;
+  a->m = m;
+  a->fold = 32;
   for (uint32_t r = 0; r < s->R; ++r) {
     const uint32_t q = s->q[r];
-    a.lc.q[r] = q;
-    a.lc.c[r] = (uint32_t)((((uint64_t)1) << 32) % q);
-    a.lc.mu[r] = ~(uint64_t)0 / q;
+    a->lc.q[r] = q;
+    a->lc.c[r] = (uint32_t)((((uint64_t)1) << 32) % q);
+    a->lc.mu[r] = ~(uint64_t)0 / q;
     const uint32_t f = pirscan::rowsel_fold_period(q);
-    if (f < a.fold) a.fold = f;
+    if (f < a->fold) a->fold = f;
   }
+  return true;
+}
+
+size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m) {
+  pirscan::RowselLaunch a;
+  uint64_t dbw, ctw, ow;
+  if (!rowsel_launch_desc(s, m, nullptr, nullptr, nullptr, &a, &dbw, &ctw, &ow)) return 0;
+  if (!pirscan::rowsel_mfma_eligible(a, s->R)) return 0;
+  return pirscan::rowsel_mfma_workspace_bytes(a.P, m, s->D0, s->D1);
+}
+
+int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint32_t* ct,
+                           const uint32_t* db_tiled, uint32_t* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  pirscan::RowselLaunch a;
+  uint64_t dbw = 0, ctw = 0, ow = 0;
+  if (!ct || !db_tiled || !out || !rowsel_launch_desc(s, m, ct, db_tiled, out, &a, &dbw, &ctw, &ow))
+    return PIRSCAN_EINVAL;
+  if (overlap(out, ow * 4, ct, ctw * 4) || overlap(out, ow * 4, db_tiled, dbw * 4)) return PIRSCAN_EINVAL;
+  const bool mfma = pirscan::rowsel_mfma_eligible(a, s->R);
+  size_t need = 0;
+  if (mfma) {
+    need = pirscan::rowsel_mfma_workspace_bytes(a.P, m, s->D0, s->D1);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % 16) != 0)
+      return PIRSCAN_EINVAL;
+    if (overlap(workspace, need, ct, ctw * 4) || overlap(workspace, need, db_tiled, dbw * 4) ||
+        overlap(workspace, need, out, ow * 4))
+      return PIRSCAN_EINVAL;
+  }
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  if (mfma) return device_status(pirscan::launch_rowsel_mfma(a, s->R, workspace, (hipStream_t)stream));
   return device_status(pirscan::launch_rowsel(a, (hipStream_t)stream));
 }
 

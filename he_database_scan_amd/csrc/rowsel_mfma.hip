@@ -1,0 +1,292 @@
+// rowsel_mfma.hip -- batched RowSel on int8 MFMA (gfx950).
+//
+// For a batch of m >= 16 ciphertext polynomials the per-point product
+// C[mi][n] = sum_k A[mi][k] * B[k][n] (A = ct, B = DB, all values < q) is a
+// dense contraction, so it runs on v_mfma_i32_16x16x64_i8 instead of the
+// 32x32->64-bit VALU multiply (GPIR: "Enabling Practical Private Information
+// Retrieval with GPUs" observes that batching raises RowSel's arithmetic
+// intensity; VIPIR section 4.1 emulates a wide integer product with INT8
+// tensor-core GEMMs on split operands and section 4.2 discusses the modular
+// GEMM's reduction overhead).
+//
+// Every value x < q is first centred, v = x - q if x > q/2 (so |v| <= q/2 <
+// 2^30 when q < 2^31), then written in four signed 8-bit limbs
+// v = sum_i v_i 2^(8i), v_i in [-128, 127] (the bytes of
+// (v + 0x80808080) ^ 0x80808080).  Then
+//
+//   sum_k a_k b_k = sum_{d=0..6} 2^(8d) S_d,  S_d = sum_{i+j=d} sum_k a_{k,i} b_{k,j}
+//
+// exactly; each S_d is an int32 accumulation of at most four limb GEMMs with
+// |S_d| <= 4 * D0 * 2^14, which fits for D0 <= 16384.  The epilogue folds the
+// seven diagonals into one residue: sum_d (S_d + 2^31) (2^(8d) mod q) plus a
+// precomputed correction for the offsets, with the same hi*(2^32 mod q) + lo
+// fold as the VALU scan, and one Barrett reduction.
+//
+// Data movement:
+//  * ct is relaid per query (two small passes into the caller's workspace):
+//    a transpose to [p][mi][k] and a limb split into MFMA A-fragment order, so
+//    each wavefront loads its A fragments as 16-byte vectors.
+//  * The DB stays in the scan layout [p][k][n].  Lane (li, lg) of a B fragment
+//    needs 16 consecutive k of column n0+li; it loads them as 16 dwords (each
+//    load instruction covers 64-byte runs of 4 k-rows) and splits them into the
+//    four limb fragments in registers.  Two column tiles are interleaved so each
+//    128-byte row line is read by back-to-back requests.
+//  * Results are written per point, [p][mi][n] (contiguous 64-byte runs), and
+//    a transpose pass produces the p-major [mi][n][p] output.
+#include <hip/hip_runtime.h>
+
+#include "internal.hpp"
+
+namespace pirscan {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+
+// Centred signed-limb digits of a residue x < q (the byte vector of the
+// centred value's four signed 8-bit digits).
+__device__ __forceinline__ uint32_t centred_digits(uint32_t x, uint32_t q, uint32_t half) {
+  const uint32_t v = x > half ? x - q : x;  // two's complement of x - q when negative
+  return (v + 0x80808080u) ^ 0x80808080u;
+}
+
+// Four words -> four dwords, dword j holding byte j of words 0..3 (in order).
+__device__ __forceinline__ void bytes_transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                                 uint32_t o[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = ((a >> (8 * j)) & 0xFFu) | (((b >> (8 * j)) & 0xFFu) << 8) |
+           (((c >> (8 * j)) & 0xFFu) << 16) | (((d >> (8 * j)) & 0xFFu) << 24);
+}
+
+// 16 digit words (k = 0..15 of one row or column) -> 4 limb fragments.
+__device__ __forceinline__ void limb_fragments(const uint32_t w[16], v4i f[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    uint32_t o[4];
+    bytes_transpose4(w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3], o);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j][u] = (int)o[j];
+  }
+}
+
+// ct_t [P][m][D0] -> A fragments [p][s][mt][limb][lane] (16 bytes each) for
+// rows m_base .. m_base + 16*MT of this pass; zero past m and past D0.
+__global__ __launch_bounds__(kThreads) void rowsel_limbs_kernel(const uint32_t* __restrict__ ct_t,
+                                                                v4i* __restrict__ limbs, uint64_t P,
+                                                                uint32_t m, uint32_t D0, uint32_t m_base,
+                                                                uint32_t MT, uint32_t S, uint32_t N,
+                                                                LimbConsts lc) {
+  const uint64_t total = P * S * MT * 64;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t e = (uint64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const uint32_t lane = (uint32_t)(e % 64);
+    uint64_t rest = e / 64;
+    const uint32_t mt = (uint32_t)(rest % MT);
+    rest /= MT;
+    const uint32_t s = (uint32_t)(rest % S);
+    const uint64_t p = rest / S;
+    const uint32_t li = lane % 16, lg = lane / 16;
+    const uint32_t mi = m_base + mt * 16 + li;
+    const uint32_t q = lc.q[p / N], half = q / 2;
+    uint32_t w[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t k = s * 64 + lg * 16 + t;
+      const uint32_t x = (mi < m && k < D0) ? ct_t[(p * m + mi) * D0 + k] : 0u;
+      w[t] = centred_digits(x, q, half);  // x = 0 gives digit bytes 0
+    }
+    v4i f[4];
+    limb_fragments(w, f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) limbs[((((p * S + s) * MT + mt) * 4 + j) * 64) + lane] = f[j];
+  }
+}
+
+struct MfmaEpilogue {
+  uint32_t w[kMaxLimbs][7];  // 2^(8d) mod q
+  uint32_t corr[kMaxLimbs];  // -(2^31 * sum_d w_d) mod q: undoes the +2^31 offsets
+};
+
+// One wavefront = one point and NTW column tiles of 16; MT row tiles of 16.
+template <int MT, int NTW>
+__global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, MfmaEpilogue ep,
+                                                               const v4i* __restrict__ limbs,
+                                                               uint32_t* __restrict__ out_t,
+                                                               uint32_t m_base, uint32_t nblk,
+                                                               uint64_t items, uint32_t S) {
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t li = lane % 16, lg = lane / 16;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const uint64_t item = (uint64_t)wg * (kThreads / 64) + wave;
+  if (item >= items) return;  // no barriers in this kernel
+  const uint64_t p = item / nblk;
+  const uint32_t n0 = (uint32_t)(item % nblk) * NTW * 16;
+  const uint32_t limb = (uint32_t)(p / a.N);
+  const uint32_t q = a.lc.q[limb], half = q / 2;
+  const uint32_t D0 = a.D0, D1 = a.D1;
+
+  // column of this lane in each tile, clamped (results past D1 are not stored)
+  const uint32_t* dbp = a.dbt + p * (uint64_t)D0 * D1;
+  uint32_t col[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const uint32_t c = n0 + nt * 16 + li;
+    col[nt] = c < D1 ? c : D1 - 1;
+  }
+
+  v4i acc[7][MT][NTW];
+#pragma unroll
+  for (int d = 0; d < 7; ++d)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) acc[d][mt][nt] = v4i{0, 0, 0, 0};
+
+  const v4i* lp = limbs + (p * S) * MT * 4 * 64 + lane;
+  for (uint32_t s = 0; s < S; ++s) {
+    v4i af[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af[mt][j] = lp[(((uint64_t)s * MT + mt) * 4 + j) * 64];
+    // 16 consecutive k of each column; past D0 the A limbs are zero, so any
+    // valid row serves
+    uint32_t w[NTW][16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      uint32_t k = s * 64 + lg * 16 + t;
+      k = k < D0 ? k : D0 - 1;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) w[nt][t] = dbp[(uint64_t)k * D1 + col[nt]];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) w[nt][t] = centred_digits(w[nt][t], q, half);
+      v4i bf[4];
+      limb_fragments(w[nt], bf);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i + j][mt][nt] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt][i], bf[j], acc[i + j][mt][nt], 0, 0, 0);
+    }
+  }
+
+  // Epilogue.  D element e of lane l is (row 4*(l/16) + e, column l%16).
+  const uint64_t c32 = a.lc.c[limb], mu = a.lc.mu[limb];
+  const uint32_t mrows = a.m - m_base;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t row = mt * 16 + 4 * lg + e;
+      if (row >= mrows) continue;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const uint32_t c = n0 + nt * 16 + li;
+        if (c >= D1) continue;
+        uint64_t x = ep.corr[limb];
+#pragma unroll
+        for (int d = 0; d < 7; ++d) {
+          x = (x >> 32) * c32 + (uint32_t)x;  // <= (2^32-1)(c32+1) < 2^63
+          x += (uint64_t)((uint32_t)acc[d][mt][nt][e] + 0x80000000u) * ep.w[limb][d];
+        }
+        uint64_t r = x - __umul64hi(x, mu) * q;
+        if (r >= q) r -= q;
+        out_t[((uint64_t)p * a.m + m_base + row) * D1 + c] = (uint32_t)r;
+      }
+    }
+  }
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+struct MfmaWs {
+  uint64_t ct_t, limbs, out_t, total;  // byte offsets / size
+};
+
+MfmaWs mfma_workspace(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1) {
+  const uint64_t S = (D0 + 63) / 64;
+  const uint32_t mt_max = m >= 32 ? 2 : (m + 15) / 16;
+  MfmaWs w{};
+  w.ct_t = 0;
+  w.limbs = align256(4ull * P * m * D0);
+  w.out_t = w.limbs + align256(P * S * mt_max * 4 * 64 * 16);
+  w.total = w.out_t + align256(4ull * P * m * D1);
+  return w;
+}
+
+template <int MT, int NTW>
+hipError_t launch_mfma_pass(const RowselLaunch& a, const MfmaEpilogue& ep, const v4i* limbs,
+                            uint32_t* out_t, uint32_t m_base, uint32_t S, hipStream_t stream) {
+  const uint32_t nblk = (a.D1 + NTW * 16 - 1) / (NTW * 16);
+  const uint64_t items = a.P * nblk;
+  const uint64_t grid = (items + 3) / 4;
+  if (grid == 0 || grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((rowsel_mfma_kernel<MT, NTW>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, a,
+                     ep, limbs, out_t, m_base, nblk, items, S);
+  return hipGetLastError();
+}
+
+uint32_t grid_for(uint64_t items) {
+  uint64_t g = (items + kThreads - 1) / kThreads;
+  if (g > (1u << 20)) g = 1u << 20;
+  return (uint32_t)(g ? g : 1);
+}
+
+}  // namespace
+
+bool rowsel_mfma_eligible(const RowselLaunch& a, uint32_t R) {
+  if (a.m < kRowselMfmaMinRows || a.D0 > 16384) return false;
+  for (uint32_t r = 0; r < R; ++r)
+    if (a.lc.q[r] >= (1u << 31)) return false;
+  return true;
+}
+
+size_t rowsel_mfma_workspace_bytes(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1) {
+  return (size_t)mfma_workspace(P, m, D0, D1).total;
+}
+
+hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace, hipStream_t stream) {
+  const MfmaWs ws = mfma_workspace(a.P, a.m, a.D0, a.D1);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  uint32_t* ct_t = reinterpret_cast<uint32_t*>(base + ws.ct_t);
+  v4i* limbs = reinterpret_cast<v4i*>(base + ws.limbs);
+  uint32_t* out_t = reinterpret_cast<uint32_t*>(base + ws.out_t);
+  const uint32_t S = (a.D0 + 63) / 64;
+
+  MfmaEpilogue ep{};
+  for (uint32_t r = 0; r < R; ++r) {
+    const uint64_t q = a.lc.q[r];
+    uint64_t sum = 0;
+    for (int d = 0; d < 7; ++d) {
+      ep.w[r][d] = (uint32_t)((((unsigned __int128)1) << (8 * d)) % q);
+      sum += ep.w[r][d];
+    }
+    const uint64_t off = (uint64_t)(((unsigned __int128)(1ull << 31) * sum) % q);
+    ep.corr[r] = (uint32_t)((q - off) % q);
+  }
+
+  // ct [m*D0][P] -> ct_t [P][m*D0]
+  hipError_t e = launch_layout_db(a.ct, ct_t, (uint64_t)a.m * a.D0, a.P, stream);
+  if (e != hipSuccess) return e;
+  for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
+    const uint32_t rows = a.m - m_base;
+    const uint32_t MT = rows > 16 ? 2 : 1;
+    hipLaunchKernelGGL(rowsel_limbs_kernel, dim3(grid_for(a.P * S * MT * 64)), dim3(kThreads), 0, stream,
+                       ct_t, limbs, a.P, a.m, a.D0, m_base, MT, S, a.N, a.lc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (MT == 2) e = launch_mfma_pass<2, 2>(a, ep, limbs, out_t, m_base, S, stream);
+    else e = launch_mfma_pass<1, 2>(a, ep, limbs, out_t, m_base, S, stream);
+    if (e != hipSuccess) return e;
+  }
+  // out_t [P][m*D1] -> out [m*D1][P]
+  return launch_layout_db(out_t, a.out, a.P, (uint64_t)a.m * a.D1, stream);
+}
+
+}  // namespace pirscan

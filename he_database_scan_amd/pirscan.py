@@ -67,7 +67,9 @@ def _load():
         L.pirscan_layout_db_bytes.restype = sz
         L.pirscan_layout_db.argtypes = [shp, vp, vp, vp]
         L.pirscan_layout_db.restype = ctypes.c_int
-        L.pirscan_rowsel_modgemm.argtypes = [shp, u32, vp, vp, vp, vp]
+        L.pirscan_rowsel_workspace_bytes.argtypes = [shp, u32]
+        L.pirscan_rowsel_workspace_bytes.restype = sz
+        L.pirscan_rowsel_modgemm.argtypes = [shp, u32, vp, vp, vp, vp, sz, vp]
         L.pirscan_rowsel_modgemm.restype = ctypes.c_int
         L.pirscan_scalar_workspace_bytes.argtypes = [u64, u64, u32]
         L.pirscan_scalar_workspace_bytes.restype = sz
@@ -140,15 +142,24 @@ def layout_db(shape: RowselShape, db_pmajor, db_tiled, stream=None) -> None:
            _load().pirscan_layout_db(ctypes.byref(shape), _ptr(db_pmajor), _ptr(db_tiled), _stream(stream)))
 
 
-def rowsel_modgemm(shape: RowselShape, m: int, ct, db_tiled, out, stream=None) -> None:
-    """out[m][D1][P] = RowSel(ct[m][D0][P], db) mod q, on device."""
+def rowsel_workspace_bytes(shape: RowselShape, m: int) -> int:
+    return int(_load().pirscan_rowsel_workspace_bytes(ctypes.byref(shape), m))
+
+
+def rowsel_modgemm(shape: RowselShape, m: int, ct, db_tiled, out, workspace=None, stream=None) -> None:
+    """out[m][D1][P] = RowSel(ct[m][D0][P], db) mod q, on device.
+
+    ``workspace``: a device buffer of at least ``rowsel_workspace_bytes(shape, m)``
+    bytes (any dtype; may be None when that size is 0), owned by the caller.
+    """
     P = shape.P
     _dev(ct, "ct", 4, m * shape.D0 * P)
     _dev(db_tiled, "db_tiled", 4, shape.D0 * shape.D1 * P)
     _dev(out, "out", 4, m * shape.D1 * P)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pirscan_rowsel_modgemm",
            _load().pirscan_rowsel_modgemm(ctypes.byref(shape), m, _ptr(ct), _ptr(db_tiled), _ptr(out),
-                                          _stream(stream)))
+                                          _ptr(workspace), wbytes, _stream(stream)))
 
 
 def scalar_workspace_bytes(M: int, K: int, B: int) -> int:

@@ -88,18 +88,33 @@ int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor,
                       uint32_t* db_tiled, void* stream);
 
 /*
+ * Workspace bytes pirscan_rowsel_modgemm needs for (shape, m): 0 when the
+ * batch runs on the VALU path (m < 16, a modulus >= 2^31, or D0 > 16384),
+ * else room for the per-query relayout of ct and of the output used by the
+ * int8-MFMA path (GPIR: batching makes RowSel a dense contraction).  0 also
+ * on an invalid shape.
+ */
+size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m);
+
+/*
  * RowSel scan: out[mi][n][p] = (sum_k ct[mi][k][p] * db[k][n][p]) mod q[p/N].
- *   m        : ciphertext polynomials in the query batch (m = 2B for B BFV
- *              ciphertexts of two polynomials each), m >= 1.
- *   ct       : [m][D0][P] uint32, p-major, entries < q[p/N].
- *   db_tiled : output of pirscan_layout_db for the same shape.
- *   out      : [m][D1][P] uint32, p-major, canonical residues in [0, q[p/N]).
+ *   m         : ciphertext polynomials in the query batch (m = 2B for B BFV
+ *               ciphertexts of two polynomials each), m >= 1.
+ *   ct        : [m][D0][P] uint32, p-major, entries < q[p/N].
+ *   db_tiled  : output of pirscan_layout_db for the same shape.
+ *   out       : [m][D1][P] uint32, p-major, canonical residues in [0, q[p/N]).
+ *   workspace : >= pirscan_rowsel_workspace_bytes(s, m) bytes of device
+ *               memory, 16-byte aligned, owned by the caller (may be NULL with
+ *               workspace_bytes 0 when that size is 0); contents ignored on
+ *               entry and unspecified on return.
  * Entries >= q are a precondition violation (not checked; the result is then
- * unspecified but memory-safe).  `out` must not overlap ct or db_tiled.
+ * unspecified but memory-safe).  `out` and `workspace` must not overlap ct,
+ * db_tiled or each other.
  */
 int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m,
                            const uint32_t* ct, const uint32_t* db_tiled,
-                           uint32_t* out, void* stream);
+                           uint32_t* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Workspace bytes pirscan_scalar_gemm_u32 needs for (M, K, B): the signed
  * digit planes of the query plus split-K partial sums.  0 on invalid sizes. */

@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("pirscan_layout_db", "pirscan_rowsel_modgemm", "pirscan_scalar_gemm_u32",
+    for want in ("pirscan_layout_db", "pirscan_rowsel_modgemm", "pirscan_rowsel_workspace_bytes",
+                 "pirscan_scalar_gemm_u32",
                  "pirscan_scalar_workspace_bytes", "pirscan_layout_db_bytes", "pirscan_strerror",
                  "pirscan_version", "pirscan_last_device_error"):
         assert want in names
@@ -75,6 +76,19 @@ def test_page_size_identities():
     assert (1 << 16) * 4 == sizes["scalar_query_d0_65536"]
 
 
+def test_rowsel_workspace_sizes():
+    s = pirscan.RowselShape.make(4096, Q3, 1024, 1024)
+    assert pirscan.rowsel_workspace_bytes(s, 2) == 0            # VALU path, no workspace
+    assert pirscan.rowsel_workspace_bytes(s, 15) == 0
+    P = 12288
+    ct = out = 4 * P * 32 * 1024
+    limbs = P * 16 * 2 * 4 * 64 * 16                            # 16 k-steps, 2 row tiles, 4 limbs
+    assert pirscan.rowsel_workspace_bytes(s, 32) == ct + limbs + out
+    big_q = pirscan.RowselShape.make(16, [2147483659], 64, 64)  # a modulus >= 2^31: VALU path
+    assert pirscan.rowsel_workspace_bytes(big_q, 32) == 0
+    assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(16, Q3, 20000, 64), 32) == 0
+
+
 def test_scalar_workspace_sizes():
     # B=1: 4 digit bytes per k (k padded to 4096) + split-K partials
     assert pirscan.scalar_workspace_bytes(32768, 32768, 1) == 32768 * 4 + 8 * 32768 * 4
@@ -85,10 +99,11 @@ def test_scalar_workspace_sizes():
     assert pirscan.scalar_workspace_bytes(5, 17, 1) == 0                    # generic path
 
 
-def _call_rowsel(shape, m, ct, db, out):
+def _call_rowsel(shape, m, ct, db, out, ws=0, ws_bytes=0):
     L = pirscan.lib()
     return L.pirscan_rowsel_modgemm(ctypes.byref(shape) if shape is not None else None, m,
-                                    ctypes.c_void_p(ct), ctypes.c_void_p(db), ctypes.c_void_p(out), None)
+                                    ctypes.c_void_p(ct), ctypes.c_void_p(db), ctypes.c_void_p(out),
+                                    ctypes.c_void_p(ws), ws_bytes, None)
 
 
 def test_rowsel_rejects_bad_arguments_without_a_device():
@@ -103,6 +118,15 @@ def test_rowsel_rejects_bad_arguments_without_a_device():
     assert _call_rowsel(s, 2, A, B, B + 64) == pirscan.EINVAL     # out overlaps db
     bad = pirscan.RowselShape.make(8, [1], 4, 4)
     assert _call_rowsel(bad, 2, A, B, C) == pirscan.EINVAL
+    # the batched (MFMA) path needs its workspace
+    big = pirscan.RowselShape.make(8, Q3, 64, 32)
+    need = pirscan.rowsel_workspace_bytes(big, 32)
+    W = 1 << 44
+    assert need > 0
+    assert _call_rowsel(big, 32, A, B, C) == pirscan.EINVAL                     # no workspace
+    assert _call_rowsel(big, 32, A, B, C, W, need - 1) == pirscan.EINVAL        # too small
+    assert _call_rowsel(big, 32, A, B, C, W + 8, need) == pirscan.EINVAL        # misaligned
+    assert _call_rowsel(big, 32, A, B, C, C + 64, need) == pirscan.EINVAL       # overlaps out
     L = pirscan.lib()
     assert L.pirscan_layout_db(ctypes.byref(s), ctypes.c_void_p(A), ctypes.c_void_p(A + 16), None) == pirscan.EINVAL
 

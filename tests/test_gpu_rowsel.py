@@ -22,8 +22,15 @@ def run_gpu(ct, db, N, q):
     d_dbt = empty_u32(db.shape)
     pirscan.layout_db(shape, d_db, d_dbt)
     d_out = empty_u32((m, D1, P))
-    pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out)
+    pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out, workspace(shape, m))
     return to_host_u32(d_out)
+
+
+def workspace(shape, m):
+    import torch
+
+    n = pirscan.rowsel_workspace_bytes(shape, m)
+    return torch.empty(n, dtype=torch.uint8, device="cuda:0") if n else None
 
 
 def rand_res(rng, shape, N, q):
@@ -51,7 +58,7 @@ def test_tiny_one_hot_rows_and_all_max():
     for k in range(D0):
         ct = np.zeros((m, D0, P), dtype=np.uint32)
         ct[:, k, :] = 1
-        pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out)
+        pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out, workspace(shape, m))
         got = to_host_u32(d_out)
         for mi in range(m):
             np.testing.assert_array_equal(got[mi], db[k])
@@ -130,7 +137,7 @@ def sampled_full_size(seed, D0, D1, m, points, ct_stream=synth.STREAM_ROWSEL_CT)
         synth.fill_residues_(d_ct, seed, ct_stream, N, q)
         d_out = empty_u32((mm, D1, P))
         say(f"  scan m={mm}")
-        pirscan.rowsel_modgemm(shape, mm, d_ct, d_dbt, d_out)
+        pirscan.rowsel_modgemm(shape, mm, d_ct, d_dbt, d_out, workspace(shape, mm))
         pts = torch.tensor(points, device=d_out.device)
         outs[mm] = to_host_u32(d_out.index_select(2, pts))
         del d_ct, d_out
@@ -159,3 +166,25 @@ def test_large_config_sampled():
     """48 GiB DB, B=1 (m=2) and B=16 (m=32) sharing one tiled DB."""
     pts = [0, 1, 2, 3, 4095, 4096, 4097, 9000, 12286, 12287]
     sampled_full_size(4, 1024, 1024, [2, 32], pts)
+
+
+# Batched path (m >= 16, every q < 2^31: int8 MFMA over centred signed limbs)
+@pytest.mark.parametrize("q,m,D0,D1", [([2147483647, 2147483629], 16, 100, 50),
+                                       ([2147483647], 32, 130, 33), ([1073741827, 65537], 40, 64, 96),
+                                       (MED_Q, 32, 1, 16), ([3, 5], 17, 257, 40)])
+def test_batched_path_edges(q, m, D0, D1):
+    N = 4
+    P = N * len(q)
+    shape = pirscan.RowselShape.make(N, q, D0, D1)
+    assert pirscan.rowsel_workspace_bytes(shape, m) > 0
+    rng = np.random.default_rng(m * 7 + D0)
+    say(f"rowsel batched q={q} m={m} D0={D0} D1={D1}")
+    ct = rand_res(rng, (m, D0, P), N, q)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))
+    qv = np.asarray(q, dtype=np.uint64)[np.arange(P) // N]
+    # the centring boundary: values q/2 and q/2 + 1, and q - 1
+    for vals in ((qv // 2), (qv // 2 + 1) % qv, qv - 1):
+        ctv = np.broadcast_to(vals.astype(np.uint32), (m, D0, P)).copy()
+        dbv = np.broadcast_to(((qv - 1) - vals % qv).astype(np.uint32), (D0, D1, P)).copy()
+        np.testing.assert_array_equal(run_gpu(ctv, dbv, N, q), oracle.rowsel(ctv, dbv, N, q))
