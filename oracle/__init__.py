@@ -11,6 +11,9 @@ This module is argument marshalling around ``liboracle.so`` (plain C, built by
 * :func:`rowsel` -- GPIR's RowSel, ``out[p,m,n] = sum_k ct[p,m,k] * DB[p,k,n]
   mod q_r`` (GPIR, the RowSel formulation paragraph; VIPIR section 4 and 2.3),
   in p-major layouts, exact 128-bit accumulation.
+* :func:`exppack` -- VIPIR's ExpPack packing GEMM ``H*C + (0|G) mod q_r``
+  (VIPIR section 3.5.2), the (#RNS*N)-parallel modular GEMM with the body
+  term added to each client's second column.
 * :func:`scalar` -- VIPIR's INT8 x INT32 database GEMM mod 2^32 (VIPIR section
   2.5 and section 4), sign-extended DB bytes.
 * number-theory helpers (prime search, primitive roots, direct-evaluation
@@ -51,6 +54,10 @@ def lib():
         L.oracle_rowsel.argtypes = [_u32p, _u32p, _u32p, ctypes.c_uint32, ctypes.c_uint32, _u32p,
                                     ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int]
         L.oracle_rowsel.restype = ctypes.c_int
+        L.oracle_exppack.argtypes = [_u32p, _u32p, _u32p, _u32p, ctypes.c_uint32, ctypes.c_uint32,
+                                     _u32p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                     ctypes.c_int]
+        L.oracle_exppack.restype = ctypes.c_int
         L.oracle_scalar.argtypes = [_i8p, _u32p, _u32p, ctypes.c_uint64, ctypes.c_uint64,
                                     ctypes.c_uint32, ctypes.c_int]
         L.oracle_scalar.restype = ctypes.c_int
@@ -105,6 +112,34 @@ def rowsel(ct, db, N: int, q, nthreads: int = 0) -> np.ndarray:
                              _ptr(q, _u32p), m, D0, D1, int(nthreads))
     if rc != 0:
         raise ValueError("oracle_rowsel failed (zero modulus?)")
+    return out
+
+
+def exppack(H, C, G, N: int, q, nthreads: int = 0) -> np.ndarray:
+    """ExpPack's H*C + (0|G) on p-major arrays (VIPIR section 3.5.2).
+
+    H [Dr][n][P], C [n][2B][P], G [Dr][B][P] or None -> out [Dr][2B][P];
+    point p uses modulus q[p // N].
+    """
+    H = _u32(H)
+    C = _u32(C)
+    q = _u32(q)
+    Dr, n, P = H.shape
+    nb, cols, Pb = C.shape
+    if nb != n or Pb != P or cols % 2 or P != len(q) * N:
+        raise ValueError("exppack: inconsistent shapes")
+    B = cols // 2
+    gp = None
+    if G is not None:
+        G = _u32(G)
+        if G.shape != (Dr, B, P):
+            raise ValueError("exppack: G must be [Dr][B][P]")
+        gp = _ptr(G, _u32p)
+    out = np.empty((Dr, cols, P), dtype=np.uint32)
+    rc = lib().oracle_exppack(_ptr(H, _u32p), _ptr(C, _u32p), gp, _ptr(out, _u32p), N, len(q),
+                              _ptr(q, _u32p), Dr, n, B, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_exppack failed (zero modulus?)")
     return out
 
 

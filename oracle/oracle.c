@@ -5,7 +5,8 @@
  *
  * Style rule for this file: each function is the definition written out as
  * loops, in the pages' index order.  Threads split only the outermost
- * independent index (points for RowSel, rows for the scalar product); they
+ * independent index (points for RowSel and ExpPack, rows for the scalar
+ * product); they
  * never change the order or the exactness of any sum.
  */
 #include "oracle.h"
@@ -83,6 +84,67 @@ int oracle_rowsel(const uint32_t *ct, const uint32_t *db, uint32_t *out,
   }
   for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, rowsel_worker, &jobs[t]);
   rowsel_worker(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* ExpPack packing GEMM H*C + (0|G)                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const uint32_t *H, *C, *G;
+  uint32_t *out;
+  uint32_t N, Dr, n, B;
+  uint64_t P;
+  const uint32_t *q;
+  uint64_t p_begin, p_end;
+} exppack_job;
+
+static void *exppack_worker(void *arg) {
+  const exppack_job *j = (const exppack_job *)arg;
+  const uint64_t P = j->P, cols = 2ull * j->B;
+  for (uint64_t p = j->p_begin; p < j->p_end; ++p) {
+    const uint64_t qr = j->q[p / j->N];
+    for (uint32_t r = 0; r < j->Dr; ++r) {
+      for (uint64_t c = 0; c < cols; ++c) {
+        u128 acc = 0;
+        for (uint32_t i = 0; i < j->n; ++i) {
+          const uint64_t h = j->H[((uint64_t)r * j->n + i) * P + p];
+          const uint64_t x = j->C[((uint64_t)i * cols + c) * P + p];
+          acc += (u128)h * x;
+        }
+        /* (0 | G): the second column of client c/2 carries G */
+        if (j->G && (c & 1)) acc += j->G[((uint64_t)r * j->B + c / 2) * P + p];
+        j->out[((uint64_t)r * cols + c) * P + p] = (uint32_t)(acc % qr);
+      }
+    }
+  }
+  return NULL;
+}
+
+int oracle_exppack(const uint32_t *H, const uint32_t *C, const uint32_t *G,
+                   uint32_t *out, uint32_t N, uint32_t R, const uint32_t *q,
+                   uint32_t Dr, uint32_t n, uint32_t B, int nthreads) {
+  if (!H || !C || !out || !q || N == 0 || R == 0) return -1;
+  for (uint32_t r = 0; r < R; ++r)
+    if (q[r] == 0) return -1;
+  const uint64_t P = (uint64_t)R * N;
+  nthreads = clamp_threads(nthreads, P);
+  pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+  exppack_job *jobs = (exppack_job *)calloc((size_t)nthreads, sizeof(exppack_job));
+  if (!th || !jobs) { free(th); free(jobs); return -1; }
+  for (int t = 0; t < nthreads; ++t) {
+    exppack_job *j = &jobs[t];
+    j->H = H; j->C = C; j->G = G; j->out = out;
+    j->N = N; j->Dr = Dr; j->n = n; j->B = B; j->P = P; j->q = q;
+    j->p_begin = P * (uint64_t)t / (uint64_t)nthreads;
+    j->p_end = P * (uint64_t)(t + 1) / (uint64_t)nthreads;
+  }
+  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, exppack_worker, &jobs[t]);
+  exppack_worker(&jobs[0]);
   for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
   free(th);
   free(jobs);

@@ -63,6 +63,25 @@ int oracle_scalar(const int8_t *db, const uint32_t *Q, uint32_t *out,
                   uint64_t M, uint64_t K, uint32_t B, int nthreads);
 
 /*
+ * ExpPack packing GEMM [VIPIR section 3.5.2: after the NTT the packing step
+ * H*C + (0|G) is a (#RNS*N)-parallel ceil(D1/N) x 2B x n INT32 GEMM with a
+ * modular reduction; section 3.6 gives its sizes]:
+ *
+ *   out[r][j][p] = ( sum_{i<n} H[r][i][p] * C[i][j][p] + Z[r][j][p] ) mod q[p / N]
+ *   Z[r][2b][p] = 0,  Z[r][2b+1][p] = G[r][b][p]
+ *
+ * for r < Dr (= ceil(D1/N) output ciphertexts), j < 2B, p < P = R*N.  H is the
+ * Dr x n hint matrix, C the n x 2B matrix of expanded special ciphertexts
+ * (client b owns columns 2b, 2b+1), G the Dr x B body matrix; every matrix is
+ * row-major with p-major polynomial entries: H [Dr][n][P], C [n][2B][P],
+ * G [Dr][B][P], out [Dr][2B][P].  G may be NULL (Z = 0).  Exact unsigned
+ * 128-bit accumulation, one final reduction: out is canonical in [0, q[r]).
+ */
+int oracle_exppack(const uint32_t *H, const uint32_t *C, const uint32_t *G,
+                   uint32_t *out, uint32_t N, uint32_t R, const uint32_t *q,
+                   uint32_t Dr, uint32_t n, uint32_t B, int nthreads);
+
+/*
  * Signed-digit split of a 32-bit word [VIPIR section 4.1 splits the INT32
  * operand into four INT8 matrices; the signed reading is the one an
  * int8 x int8 datapath accepts]: digits s[0..3] in [-128, 127] with

@@ -25,7 +25,8 @@ Z_{2^32} query words):
 * int8:           byte ``i % 8`` (little-endian) of ``value(i // 8)``;
 * uint32:         the high 32 bits of ``value(i)``.
 
-Streams: RowSel DB 1, RowSel ct 2, scalar DB 3, scalar query 4.
+Streams: RowSel DB 1, RowSel ct 2, scalar DB 3, scalar query 4, ExpPack hint H 5,
+ExpPack special ciphertexts C 6, ExpPack body G 7, NTT input 8.
 """
 from __future__ import annotations
 
@@ -43,6 +44,10 @@ STREAM_ROWSEL_DB = 1
 STREAM_ROWSEL_CT = 2
 STREAM_SCALAR_DB = 3
 STREAM_SCALAR_Q = 4
+STREAM_EXPPACK_H = 5
+STREAM_EXPPACK_C = 6
+STREAM_EXPPACK_G = 7
+STREAM_NTT_IN = 8
 
 
 def mix64_int(z: int) -> int:
