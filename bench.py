@@ -11,11 +11,17 @@ The tiled RowSel DB is built once by pirscan_layout_db before timing (the DB
 is static).  All inputs are seeded synthetic data resident in HBM before the
 timed region.  ``value`` = DB bytes scanned per step / step time (GB/s,
 1 GB = 1e9 B).  Per-scan times come from HIP events on the stream the kernels
-run on; the ``roofline`` object is for the scan that takes the most time.
+run on: around each scan call, and -- through the library's kernel-timer hook
+-- around each scan's main kernel alone.  The ``roofline`` object is for the
+main kernel that takes the most time, priced with its own launch duration.
+
+Outside the step, ``next_rows`` measures VIPIR's ExpPack packing GEMM
+H*C + (0|G) (section 3.6 size: N = 2^12, 3 primes, Dr = 256, n = 1280, a
+15 GiB hint) for B = 1 and B = 16 the same way.
 
 The ``cpu_baseline`` leg times the CPU oracle (oracle/, plain C) on a bounded
 sample of each of the four scans and reports the oracle's DB-scan rate for the
-same step mix.
+same step mix (and per scan, ExpPack included).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -41,12 +47,20 @@ VALU_MAD64_PEAK_TMACS = 256 * 4 * 16 * 2.4e9 / 1e12
 RS_N, RS_Q = 4096, [536813569, 536690689, 536641537]
 RS_D0 = RS_D1 = 1024
 SC_M = SC_K = 262144
-SEEDS = {"rowsel": 4, "scalar": 5}
+EP_DR, EP_N = 256, 1280        # ExpPack: output ciphertexts, LWE dimension (same ring as RowSel)
+SEEDS = {"rowsel": 4, "scalar": 5, "exppack": 6}
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+_CSRC = os.path.join(ROOT, "he_database_scan_amd", "csrc")
+# The source file of each scan's main kernel (traffic figures are dropped once
+# that file changes).
 KERNEL_SOURCES = {
-    "rowsel": os.path.join(ROOT, "he_database_scan_amd", "csrc", "rowsel.hip"),
-    "scalar": os.path.join(ROOT, "he_database_scan_amd", "csrc", "scalar.hip"),
+    "rowsel_48GiB_B1": os.path.join(_CSRC, "rowsel.hip"),
+    "rowsel_48GiB_B16": os.path.join(_CSRC, "rowsel_mfma.hip"),
+    "scalar_64GiB_B1": os.path.join(_CSRC, "scalar.hip"),
+    "scalar_64GiB_B32": os.path.join(_CSRC, "scalar.hip"),
+    "exppack_15GiB_B1": os.path.join(_CSRC, "rowsel.hip"),
+    "exppack_15GiB_B16": os.path.join(_CSRC, "rowsel_mfma.hip"),
 }
 
 
@@ -99,6 +113,24 @@ class Workloads:
             self.sout[B] = torch.empty((SC_M, B), dtype=torch.int32, device=dev)
             self.ws[B] = torch.empty(pirscan.scalar_workspace_bytes(SC_M, SC_K, B), dtype=torch.uint8,
                                      device=dev)
+        log("setup: ExpPack 15 GiB hint (synthesise p-major, one-time relayout)")
+        self.eshape = pirscan.ExppackShape.make(RS_N, RS_Q, EP_DR, EP_N)
+        h = torch.empty((EP_DR, EP_N, P), dtype=torch.int32, device=dev)
+        synth.fill_residues_(h, SEEDS["exppack"], synth.STREAM_EXPPACK_H, RS_N, RS_Q)
+        self.ht = torch.empty((P, EP_N, EP_DR), dtype=torch.int32, device=dev)
+        pirscan.exppack_layout_h(self.eshape, h, self.ht)
+        torch.cuda.synchronize()
+        del h
+        torch.cuda.empty_cache()
+        self.ec, self.eg, self.eout, self.ews = {}, {}, {}, {}
+        for B in (1, 16):
+            self.ec[B] = torch.empty((EP_N, 2 * B, P), dtype=torch.int32, device=dev)
+            synth.fill_residues_(self.ec[B], SEEDS["exppack"], synth.STREAM_EXPPACK_C, RS_N, RS_Q)
+            self.eg[B] = torch.empty((EP_DR, B, P), dtype=torch.int32, device=dev)
+            synth.fill_residues_(self.eg[B], SEEDS["exppack"], synth.STREAM_EXPPACK_G, RS_N, RS_Q)
+            self.eout[B] = torch.empty((EP_DR, 2 * B, P), dtype=torch.int32, device=dev)
+            nws = pirscan.exppack_workspace_bytes(self.eshape, B)
+            self.ews[B] = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         torch.cuda.synchronize()
 
     # name -> (callable, DB bytes, algorithmic HBM bytes, queries, macs, kind)
@@ -120,15 +152,34 @@ class Workloads:
                 sc_db, sc_db + 4 * SC_K * B + 4 * SC_M * B, B, SC_M * SC_K * B, "scalar")
         return out
 
+    def next_scans(self):
+        """ExpPack packing GEMM (the next row beyond the step): the 15 GiB hint
+        is the streamed operand; C, G and out are per query."""
+        P = RS_N * len(RS_Q)
+        h_bytes = 4 * P * EP_DR * EP_N
+        pz = self.pirscan
+        out = {}
+        for B in (1, 16):
+            c, g, o, ws = self.ec[B], self.eg[B], self.eout[B], self.ews[B]
+            alg = h_bytes + 4 * P * (EP_N * 2 * B + EP_DR * B + EP_DR * 2 * B)
+            out[f"exppack_15GiB_B{B}"] = (
+                (lambda c=c, g=g, o=o, ws=ws, B=B: pz.exppack_modgemm(self.eshape, B, c, self.ht, g, o, ws)),
+                h_bytes, alg, B, P * EP_DR * 2 * B * EP_N, "exppack")
+        return out
+
 
 # int8 MACs the MFMA paths issue per algorithmic MAC: the scalar B>1 GEMM
-# multiplies 4 query digit planes; batched RowSel multiplies 4 x 4 limb pairs.
-MFMA_MACS_PER_MAC = {"rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4}
+# multiplies 4 query digit planes; batched RowSel / ExpPack multiply 4 x 4
+# limb pairs.
+MFMA_MACS_PER_MAC = {"rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4, "exppack_15GiB_B16": 16}
 
 
 def roofline_for(name, ms, db_bytes, alg_bytes, macs):
     """Every scan here is bound by HBM bandwidth at its shape; the MFMA scans
-    also report the int8 MFMA utilisation they need."""
+    also report the int8 MFMA utilisation they need.  ``ms`` is the main
+    kernel's launch duration; its algorithmic bytes are the scan's (the
+    streamed DB, the query operand once and the output once: the MFMA path's
+    limb and output staging have exactly the sizes of ct and out)."""
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     rf = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
           "frac": achieved / HBM_PEAK_GBS}
@@ -149,19 +200,37 @@ def traffic_for(name):
     ent = data.get(name)
     if not ent:
         return None
-    kind = "rowsel" if name.startswith("rowsel") else "scalar"
-    if ent.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
+    if ent.get("source_sha256_16") != source_hash(KERNEL_SOURCES[name]):
         return None
     return ent.get("bytes_per_launch")
 
 
-# The kernel that dominates each scan (the one the roofline and traffic refer to).
+# The main kernel of each scan (the one the kernel timer, the roofline and the
+# traffic refer to), in the order the benchmark first launches the scans.
+# RowSel and ExpPack share kernel templates; their launches differ in grid
+# size, and the scans are told apart by the (kernel, grid) group that appears
+# first in dispatch order.
 SCAN_KERNELS = {
     "rowsel_48GiB_B1": "rowsel_kernel<2,",
     "rowsel_48GiB_B16": "rowsel_mfma_kernel<2, 2>",
     "scalar_64GiB_B1": "gemv_kernel",
     "scalar_64GiB_B32": "mfma_kernel<8>",
+    "exppack_15GiB_B1": "rowsel_kernel<2,",
+    "exppack_15GiB_B16": "rowsel_mfma_kernel<2, 2>",
 }
+
+
+def assign_scan_groups(groups):
+    """groups: {(kernel, grid): first dispatch id}.  Returns {scan: (kernel,
+    grid)}, giving each scan, in SCAN_KERNELS order, the earliest group of its
+    kernel not yet taken."""
+    taken, out = set(), {}
+    for scan, pat in SCAN_KERNELS.items():
+        cands = sorted((first, g) for g, first in groups.items() if g[0].startswith(pat) and g not in taken)
+        if cands:
+            out[scan] = cands[0][1]
+            taken.add(cands[0][1])
+    return out
 
 
 def _short_kernel_name(name: str) -> str:
@@ -179,33 +248,33 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_gib: float) -> d
     import statistics
 
     def load(path, counter):
-        vals = {}
+        vals, first = {}, {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            vals.setdefault(_short_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
-        return vals
+            g = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+            vals.setdefault(g, []).append(float(r["Counter_Value"]))
+            first[g] = min(first.get(g, 1 << 62), int(r["Dispatch_Id"]))
+        return vals, first
 
     out = {"calibration": {}}
     per = {}
     for kind, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
-        vals = load(path, counter)
-        copies = [v for k, vs in vals.items() if "copy" in k.lower() for v in vs]
+        vals, first = load(path, counter)
+        copies = [v for g, vs in vals.items() if "copy" in g[0].lower() for v in vs]
         if not copies:
             raise SystemExit(f"no copy kernel in {path}: run the profile with --calib-copy-gib")
         scale = calib_gib * 2**30 / (max(copies) * 1024.0)  # true bytes per counted byte
         out["calibration"][counter] = {"copy_bytes": calib_gib * 2**30, "counter_KiB": max(copies),
                                        "scale": scale}
-        for scan, pat in SCAN_KERNELS.items():
-            hits = [v for k, vs in vals.items() if k.startswith(pat) for v in vs]
-            if hits:
-                per.setdefault(scan, {})[kind + "_bytes"] = statistics.median(hits) * 1024.0 * scale
-                per[scan]["kernel"] = [k for k in vals if k.startswith(pat)][0]
+        for scan, g in assign_scan_groups(first).items():
+            per.setdefault(scan, {})[kind + "_bytes"] = statistics.median(vals[g]) * 1024.0 * scale
+            per[scan]["kernel"] = g[0]
+            per[scan]["grid_size"] = g[1]
     for scan, ent in per.items():
         if "fetch_bytes" in ent and "write_bytes" in ent:
             ent["bytes_per_launch"] = ent["fetch_bytes"] + ent["write_bytes"]
-            kind = "rowsel" if scan.startswith("rowsel") else "scalar"
-            ent["source_sha256_16"] = source_hash(KERNEL_SOURCES[kind])
+            ent["source_sha256_16"] = source_hash(KERNEL_SOURCES[scan])
             out[scan] = ent
     return out
 
@@ -240,11 +309,27 @@ def cpu_baseline(budget_s: float = 4.0):
         Q = synth.uint32_array(SEEDS["scalar"], synth.STREAM_SCALAR_Q, (SC_K, B))
         return (lambda: oracle.scalar(db, Q, nthreads=threads)), rows * SC_K, f"{rows} rows x {SC_K}, B={B}"
 
+    def exppack_sample(B, npts):
+        pts = np.linspace(0, P - 1, npts).astype(np.uint64)
+        r = np.arange(EP_DR, dtype=np.uint64)[:, None, None]
+        i = np.arange(EP_N, dtype=np.uint64)[None, :, None]
+        H = synth.residues(SEEDS["exppack"], synth.STREAM_EXPPACK_H, (r * EP_N + i) * P + pts, P, RS_N, RS_Q)
+        ii = np.arange(EP_N, dtype=np.uint64)[:, None, None]
+        j = np.arange(2 * B, dtype=np.uint64)[None, :, None]
+        C = synth.residues(SEEDS["exppack"], synth.STREAM_EXPPACK_C, (ii * 2 * B + j) * P + pts, P, RS_N, RS_Q)
+        b = np.arange(B, dtype=np.uint64)[None, :, None]
+        G = synth.residues(SEEDS["exppack"], synth.STREAM_EXPPACK_G, (r * B + b) * P + pts, P, RS_N, RS_Q)
+        qs = [RS_Q[int(p) // RS_N] for p in pts]
+        return (lambda: oracle.exppack(H, C, G, 1, qs, nthreads=threads)), 4 * npts * EP_DR * EP_N, \
+            f"{npts} points x {EP_DR}x{EP_N}, B={B}"
+
     rates, samples = {}, []
     for name, make in (("rowsel_48GiB_B1", lambda: rowsel_sample(2, threads)),
                        ("rowsel_48GiB_B16", lambda: rowsel_sample(32, threads)),
                        ("scalar_64GiB_B1", lambda: scalar_sample(1, 4 * threads)),
-                       ("scalar_64GiB_B32", lambda: scalar_sample(32, threads))):
+                       ("scalar_64GiB_B32", lambda: scalar_sample(32, threads)),
+                       ("exppack_15GiB_B1", lambda: exppack_sample(1, threads)),
+                       ("exppack_15GiB_B16", lambda: exppack_sample(16, threads))):
         fn, nbytes, what = make()
         reps, t0 = 0, time.perf_counter()
         while True:
@@ -256,6 +341,52 @@ def cpu_baseline(budget_s: float = 4.0):
         rates[name] = reps * nbytes / dt
         samples.append(f"{name}: {what}, {reps} reps in {dt:.1f} s")
     return rates, threads, "; ".join(samples)
+
+
+def time_scans(torch, pirscan, scans, steps, warmup, stream):
+    """Runs `warmup` untimed rounds of the scans, then times `steps` rounds:
+    HIP events around each scan call and, through the library's kernel timer,
+    around each call's main kernel.  Returns (wall seconds of the timed
+    rounds, {scan: (call ms list, main-kernel ms list)})."""
+    names = list(scans)
+    for _ in range(warmup):
+        for name in names:
+            scans[name][0]()
+    torch.cuda.synchronize()
+    events = {name: [] for name in names}
+    pirscan.kernel_timer_begin(steps * len(names))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name in names:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            scans[name][0]()
+            e1.record(stream)
+            events[name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = pirscan.kernel_timer_end(steps * len(names))
+    if len(kms) != steps * len(names):
+        raise RuntimeError(f"kernel timer recorded {len(kms)} of {steps * len(names)} launches")
+    out = {}
+    for i, name in enumerate(names):
+        out[name] = ([e0.elapsed_time(e1) for e0, e1 in events[name]], kms[i::len(names)])
+    return wall, out
+
+
+def workload_entry(name, scan, call_ms, kernel_ms):
+    fn, db_bytes, alg_bytes, queries, macs, kind = scan
+    ms = sum(call_ms) / len(call_ms)
+    kms = sum(kernel_ms) / len(kernel_ms)
+    srt = sorted(call_ms)
+    rf = roofline_for(name, kms, db_bytes, alg_bytes, macs)
+    rf["traffic"] = traffic_for(name)
+    return {"ms": ms, "ms_min": srt[0], "ms_median": srt[len(srt) // 2],
+            "kernel": SCAN_KERNELS[name], "kernel_ms": kms, "kernel_ms_min": min(kernel_ms),
+            "db_GBps": db_bytes / (ms * 1e-3) / 1e9, "qps": queries / (ms * 1e-3),
+            "hbm_frac": db_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "roofline": rf}
 
 
 def main():
@@ -276,8 +407,8 @@ def main():
         print(json.dumps(res, indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the scan shards by points (RowSel) or DB rows (scalar-HE), see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); the scan would shard "
+              "by points (RowSel, ExpPack) or by DB rows (scalar-HE) with no exchange", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -298,41 +429,18 @@ def main():
         del a, b
         torch.cuda.empty_cache()
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        for fn, *_ in scans.values():
-            fn()
-    torch.cuda.synchronize()
-
-    log(f"timing {args.steps} steps")
-    events = {name: [] for name in scans}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        for name, (fn, *_rest) in scans.items():
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            events[name].append((e0, e1))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    per = {}
-    total_db = 0
-    for name, (fn, db_bytes, alg_bytes, queries, macs, kind) in scans.items():
-        ms_list = sorted(e0.elapsed_time(e1) for e0, e1 in events[name])
-        ms = sum(ms_list) / len(ms_list)
-        total_db += db_bytes
-        rf = roofline_for(name, ms, db_bytes, alg_bytes, macs)
-        rf["traffic"] = traffic_for(name)
-        per[name] = {"ms": ms, "ms_min": ms_list[0], "ms_median": ms_list[len(ms_list) // 2],
-                     "db_GBps": db_bytes / (ms * 1e-3) / 1e9, "qps": queries / (ms * 1e-3),
-                     "hbm_frac": db_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "roofline": rf}
+    log(f"warmup {args.warmup} steps, timing {args.steps} steps")
+    wall, times = time_scans(torch, w.pirscan, scans, args.steps, args.warmup, stream)
+    per = {name: workload_entry(name, scans[name], *times[name]) for name in scans}
+    total_db = sum(v[1] for v in scans.values())
     ms_per_step = wall / args.steps * 1e3
     value = total_db * args.steps / wall / 1e9
-    dominant = max(per, key=lambda k: per[k]["ms"])
+    dominant = max(per, key=lambda k: per[k]["kernel_ms"])
+
+    log("next rows: ExpPack packing GEMM")
+    nscans = w.next_scans()
+    _, ntimes = time_scans(torch, w.pirscan, nscans, args.steps, args.warmup, stream)
+    next_rows = {name: workload_entry(name, nscans[name], *ntimes[name]) for name in nscans}
 
     result = {
         "metric": "effective DB-scan GB/s and QPS at 48/64 GiB DB; % of HBM roofline",
@@ -353,8 +461,11 @@ def main():
                    "scalar": {"M": SC_M, "K": SC_K, "B": [1, 32]},
                    "hbm_frac_of_step": value / HBM_PEAK_GBS,
                    "layout_db_once_ms": w.layout_s * 1e3},
-        "roofline": dict(per[dominant]["roofline"], kernel=dominant),
+        "roofline": dict(per[dominant]["roofline"], kernel=SCAN_KERNELS[dominant], scan=dominant),
         "workloads": per,
+        "next_rows": {"exppack": {"config": {"N": RS_N, "R": len(RS_Q), "Dr": EP_DR, "n": EP_N, "B": [1, 16],
+                                             "hint_GiB": 4 * RS_N * len(RS_Q) * EP_DR * EP_N / 2**30},
+                                  "workloads": next_rows}},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on bounded samples)")

@@ -17,22 +17,62 @@ struct LimbConsts {
   uint64_t mu[kMaxLimbs];     // floor((2^64 - 1) / q): Barrett constant for the final reduction
 };
 
+// The point-wise modular GEMM out[mi][n] = sum_k ct[mi][k] * db[k][n] (+ Z)
+// mod q_{p/N} over P points.  ct and out are p-major with the given word
+// strides (the point stride is 1); the DB is in the scan layout [P][D0][D1].
+// RowSel:  ct [m][D0][P] (ct_sm = D0*P, ct_sk = P), out [m][D1][P].
+// ExpPack: ct = C^T with C [D0][m][P] (ct_sm = P, ct_sk = m*P), DB = H^T,
+//          out [D1][m][P], and Z = the body term: for odd mi,
+//          Z[mi][n] = add[(mi >> 1) * add_sb + n * add_sn + p], else 0.
+// Both kernels write the residues per point, out_t [P][m][D1] in the caller's
+// workspace (contiguous stores), and a tiled transpose produces `out`, adding
+// Z on the way.
 struct RowselLaunch {
-  const uint32_t* ct;      // [m][D0][P]
+  const uint32_t* ct;
   const uint32_t* dbt;     // [P][D0][D1]
-  uint32_t* out;           // [m][D1][P]
+  uint32_t* out;
+  uint32_t* out_t;         // staging [P][m][D1] (workspace)
+  const uint32_t* add;     // optional body term (residues < q), null for none
+  uint64_t ct_sm, ct_sk;
+  uint64_t out_sm, out_sn;
+  uint64_t add_sb, add_sn;
   uint64_t P;
   uint32_t N, D0, D1, m;
   uint32_t fold;           // products accumulated between two folds (>= 1)
   LimbConsts lc;
 };
 
-// R1: [D0*D1][P] -> [P][D0*D1] word transpose.
+// Batched word transpose: dst[b][c][r] = src[b][r][c] for b < batch,
+// r < rows, c < cols, with
+//   src(b, r, c) = b * s_batch + r * s_row + c
+//   dst(b, c, r) = b * d_batch + c * d_row + r.
+// With `add` set (the ExpPack body term) the destination's contiguous index r
+// is a point p, and odd batches b get
+//   dst += add[(b >> 1) * add_b + c * add_c + r]  mod q_{r / N}.
+struct TransposeDesc {
+  const uint32_t* src;
+  uint32_t* dst;
+  uint64_t batch, rows, cols;
+  uint64_t s_batch, s_row;
+  uint64_t d_batch, d_row;
+  const uint32_t* add;
+  uint64_t add_b, add_c;
+  uint32_t N;
+  LimbConsts lc;
+};
+hipError_t launch_transpose(const TransposeDesc& t, hipStream_t stream);
+
+// R1: [X][P] -> [P][X] word transpose (the RowSel DB layout, X = D0*D1).
 hipError_t launch_layout_db(const uint32_t* src, uint32_t* dst, uint64_t X, uint64_t P,
                             hipStream_t stream);
 
-// R2-R4: the modular GEMM scan on the VALU (any m, any q < 2^32).
-hipError_t launch_rowsel(const RowselLaunch& a, hipStream_t stream);
+// R2-R4: the modular GEMM scan on the VALU (any m, any q < 2^32).  The
+// workspace holds out_t (rowsel_valu_workspace_bytes).
+size_t rowsel_valu_workspace_bytes(uint64_t P, uint32_t m, uint32_t D1);
+hipError_t launch_rowsel(const RowselLaunch& a, void* workspace, hipStream_t stream);
+
+// out_t [P][m][D1] -> out (strided, p-major), adding the body term if any.
+hipError_t launch_out_relayout(const RowselLaunch& a, const uint32_t* out_t, hipStream_t stream);
 
 // Batched RowSel on int8 MFMA: m >= kRowselMfmaMinRows, every q < 2^31,
 // D0 <= 16384.  Needs a workspace of rowsel_mfma_workspace_bytes().
@@ -64,6 +104,12 @@ bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPl
 hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out, uint64_t M,
                          uint64_t K, uint32_t B, const ScalarPlan& plan, void* workspace,
                          hipStream_t stream);
+
+// Benchmark hook (pirscan_kernel_timer_begin / _end): when the calling
+// thread has it on, the launchers bracket their main kernel with these two
+// calls, which record a HIP event pair on `stream`.  No-ops otherwise.
+void timer_mark_start(hipStream_t stream);
+void timer_mark_stop(hipStream_t stream);
 
 // Maps a hardware workgroup id to a logical tile id so that consecutive
 // logical tiles run on the same XCD (gfx950 dispatches workgroups round-robin

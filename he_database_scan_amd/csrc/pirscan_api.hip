@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <new>
 
 #include "../../include/pirscan.h"
 #include "internal.hpp"
@@ -12,6 +13,26 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Benchmark hook state of one thread: `cap` event pairs, `count` recorded,
+// `open` while a start has no stop yet.
+struct KernelTimer {
+  bool on = false, open = false;
+  uint32_t cap = 0, count = 0;
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+};
+thread_local KernelTimer g_timer;
+
+void timer_release() {
+  for (uint32_t i = 0; i < g_timer.cap; ++i) {
+    (void)hipEventDestroy(g_timer.start[i]);
+    (void)hipEventDestroy(g_timer.stop[i]);
+  }
+  delete[] g_timer.start;
+  delete[] g_timer.stop;
+  g_timer = KernelTimer{};
+}
 
 // Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
 constexpr int kMaxDevices = 64;
@@ -64,7 +85,109 @@ bool rowsel_shape_ok(const pirscan_rowsel_shape* s, uint64_t* P, uint64_t* db_wo
   return true;
 }
 
+// Per-prime constants and the fold period shared by every modular GEMM.
+void fill_limb_consts(const uint32_t* q, uint32_t R, pirscan::RowselLaunch* a) {
+  a->fold = 32;
+  for (uint32_t r = 0; r < R; ++r) {
+    a->lc.q[r] = q[r];
+    a->lc.c[r] = (uint32_t)((((uint64_t)1) << 32) % q[r]);
+    a->lc.mu[r] = ~(uint64_t)0 / q[r];
+    const uint32_t f = pirscan::rowsel_fold_period(q[r]);
+    if (f < a->fold) a->fold = f;
+  }
+}
+
+constexpr unsigned __int128 kMaxBytes = ~(uint64_t)0 >> 1;
+
+// Validates an ExpPack shape and batch (B may be 0 when only the hint size is
+// wanted); on success returns P and the word counts of H, C, G and out.
+bool exppack_shape_ok(const pirscan_exppack_shape* s, uint32_t B, uint64_t* P, uint64_t* h_words,
+                      uint64_t* c_words, uint64_t* g_words, uint64_t* o_words) {
+  if (!s || s->N == 0 || s->R == 0 || s->R > PIRSCAN_MAX_R || s->Dr == 0 || s->n == 0) return false;
+  if (B > 0x7FFFFFFFu) return false;
+  for (uint32_t r = 0; r < s->R; ++r)
+    if (s->q[r] < 2) return false;
+  const unsigned __int128 p = (unsigned __int128)s->R * s->N;
+  const unsigned __int128 h = p * s->Dr * s->n, c = p * s->n * 2 * B, g = p * s->Dr * B,
+                          o = p * s->Dr * 2 * B;
+  if (h * 4 > kMaxBytes || c * 4 > kMaxBytes || o * 4 > kMaxBytes) return false;
+  *P = (uint64_t)p;
+  *h_words = (uint64_t)h;
+  *c_words = (uint64_t)c;
+  *g_words = (uint64_t)g;
+  *o_words = (uint64_t)o;
+  return true;
+}
+
+// ExpPack as the point-wise modular GEMM with roles swapped (ct = C^T,
+// DB = H^T, D0 = n, D1 = Dr, m = 2B) and G as the body term.
+void exppack_launch_desc(const pirscan_exppack_shape* s, uint32_t B, uint64_t P, const uint32_t* C,
+                         const uint32_t* h_tiled, const uint32_t* G, uint32_t* out,
+                         pirscan::RowselLaunch* a) {
+  *a = pirscan::RowselLaunch{};
+  const uint64_t cols = 2ull * B;
+  a->ct = C;
+  a->dbt = h_tiled;
+  a->out = out;
+  a->add = G;
+  a->ct_sm = P;  // C [n][2B][P]: column j of C is row mi = j of C^T
+  a->ct_sk = cols * P;
+  a->out_sm = P;  // out [Dr][2B][P]
+  a->out_sn = cols * P;
+  a->add_sb = P;  // G [Dr][B][P]
+  a->add_sn = (uint64_t)B * P;
+  a->P = P;
+  a->N = s->N;
+  a->D0 = s->n;
+  a->D1 = s->Dr;
+  a->m = (uint32_t)cols;
+  fill_limb_consts(s->q, s->R, a);
+}
+
+// Workspace of the point-wise modular GEMM: the MFMA path's relayouts, or the
+// VALU path's per-point output staging.
+size_t modgemm_workspace_bytes(const pirscan::RowselLaunch& a, uint32_t R) {
+  if (pirscan::rowsel_mfma_eligible(a, R))
+    return pirscan::rowsel_mfma_workspace_bytes(a.P, a.m, a.D0, a.D1);
+  return pirscan::rowsel_valu_workspace_bytes(a.P, a.m, a.D1);
+}
+
+struct Span {
+  const void* p;
+  uint64_t bytes;
+};
+
+// Workspace checks shared by RowSel and ExpPack, then dispatch.
+int run_modgemm(const pirscan::RowselLaunch& a, uint32_t R, const Span* bufs, int nbufs, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const size_t need = modgemm_workspace_bytes(a, R);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % 16) != 0)
+    return PIRSCAN_EINVAL;
+  for (int i = 0; i < nbufs; ++i)
+    if (overlap(workspace, need, bufs[i].p, bufs[i].bytes)) return PIRSCAN_EINVAL;
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  if (pirscan::rowsel_mfma_eligible(a, R))
+    return device_status(pirscan::launch_rowsel_mfma(a, R, workspace, (hipStream_t)stream));
+  return device_status(pirscan::launch_rowsel(a, workspace, (hipStream_t)stream));
+}
+
 }  // namespace
+
+namespace pirscan {
+
+void timer_mark_start(hipStream_t stream) {
+  if (!g_timer.on || g_timer.open || g_timer.count >= g_timer.cap) return;
+  if (hipEventRecord(g_timer.start[g_timer.count], stream) == hipSuccess) g_timer.open = true;
+}
+
+void timer_mark_stop(hipStream_t stream) {
+  if (!g_timer.on || !g_timer.open) return;
+  g_timer.open = false;
+  if (hipEventRecord(g_timer.stop[g_timer.count], stream) == hipSuccess) ++g_timer.count;
+}
+
+}  // namespace pirscan
 
 extern "C" {
 
@@ -102,20 +225,16 @@ static bool rowsel_launch_desc(const pirscan_rowsel_shape* s, uint32_t m, const 
   a->ct = ct;
   a->dbt = db_tiled;
   a->out = out;
+  a->ct_sm = (uint64_t)s->D0 * P;  // ct [m][D0][P]
+  a->ct_sk = P;
+  a->out_sm = (uint64_t)s->D1 * P;  // out [m][D1][P]
+  a->out_sn = P;
   a->P = P;
   a->N = s->N;
   a->D0 = s->D0;
   a->D1 = s->D1;
   a->m = m;
-  a->fold = 32;
-  for (uint32_t r = 0; r < s->R; ++r) {
-    const uint32_t q = s->q[r];
-    a->lc.q[r] = q;
-    a->lc.c[r] = (uint32_t)((((uint64_t)1) << 32) % q);
-    a->lc.mu[r] = ~(uint64_t)0 / q;
-    const uint32_t f = pirscan::rowsel_fold_period(q);
-    if (f < a->fold) a->fold = f;
-  }
+  fill_limb_consts(s->q, s->R, a);
   return true;
 }
 
@@ -123,8 +242,7 @@ size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m)
   pirscan::RowselLaunch a;
   uint64_t dbw, ctw, ow;
   if (!rowsel_launch_desc(s, m, nullptr, nullptr, nullptr, &a, &dbw, &ctw, &ow)) return 0;
-  if (!pirscan::rowsel_mfma_eligible(a, s->R)) return 0;
-  return pirscan::rowsel_mfma_workspace_bytes(a.P, m, s->D0, s->D1);
+  return modgemm_workspace_bytes(a, s->R);
 }
 
 int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint32_t* ct,
@@ -135,20 +253,59 @@ int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint
   if (!ct || !db_tiled || !out || !rowsel_launch_desc(s, m, ct, db_tiled, out, &a, &dbw, &ctw, &ow))
     return PIRSCAN_EINVAL;
   if (overlap(out, ow * 4, ct, ctw * 4) || overlap(out, ow * 4, db_tiled, dbw * 4)) return PIRSCAN_EINVAL;
-  const bool mfma = pirscan::rowsel_mfma_eligible(a, s->R);
-  size_t need = 0;
-  if (mfma) {
-    need = pirscan::rowsel_mfma_workspace_bytes(a.P, m, s->D0, s->D1);
-    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % 16) != 0)
-      return PIRSCAN_EINVAL;
-    if (overlap(workspace, need, ct, ctw * 4) || overlap(workspace, need, db_tiled, dbw * 4) ||
-        overlap(workspace, need, out, ow * 4))
-      return PIRSCAN_EINVAL;
-  }
+  const Span ins[] = {{ct, ctw * 4}, {db_tiled, dbw * 4}, {out, ow * 4}};
+  return run_modgemm(a, s->R, ins, 3, workspace, workspace_bytes, stream);
+}
+
+size_t pirscan_exppack_layout_h_bytes(const pirscan_exppack_shape* s) {
+  uint64_t P, h, c, g, o;
+  if (!exppack_shape_ok(s, 0, &P, &h, &c, &g, &o)) return 0;
+  return (size_t)(h * 4);
+}
+
+int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_pmajor,
+                             uint32_t* h_tiled, void* stream) {
+  uint64_t P, h, c, g, o;
+  if (!exppack_shape_ok(s, 0, &P, &h, &c, &g, &o) || !h_pmajor || !h_tiled) return PIRSCAN_EINVAL;
+  if (overlap(h_pmajor, h * 4, h_tiled, h * 4)) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
-  if (mfma) return device_status(pirscan::launch_rowsel_mfma(a, s->R, workspace, (hipStream_t)stream));
-  return device_status(pirscan::launch_rowsel(a, (hipStream_t)stream));
+  // [Dr][n][P] -> [P][n][Dr]: for each hint column i, a Dr x P transpose.
+  pirscan::TransposeDesc t{};
+  t.src = h_pmajor;
+  t.dst = h_tiled;
+  t.batch = s->n;
+  t.rows = s->Dr;
+  t.cols = P;
+  t.s_batch = P;
+  t.s_row = (uint64_t)s->n * P;
+  t.d_batch = s->Dr;
+  t.d_row = (uint64_t)s->n * s->Dr;
+  return device_status(pirscan::launch_transpose(t, (hipStream_t)stream));
+}
+
+size_t pirscan_exppack_workspace_bytes(const pirscan_exppack_shape* s, uint32_t B) {
+  uint64_t P, h, c, g, o;
+  if (B == 0 || !exppack_shape_ok(s, B, &P, &h, &c, &g, &o)) return 0;
+  pirscan::RowselLaunch a;
+  exppack_launch_desc(s, B, P, nullptr, nullptr, nullptr, nullptr, &a);
+  return modgemm_workspace_bytes(a, s->R);
+}
+
+int pirscan_exppack_modgemm(const pirscan_exppack_shape* s, uint32_t B, const uint32_t* C,
+                            const uint32_t* h_tiled, const uint32_t* G, uint32_t* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  uint64_t P, hw, cw, gw, ow;
+  if (B == 0 || !C || !h_tiled || !out || !exppack_shape_ok(s, B, &P, &hw, &cw, &gw, &ow))
+    return PIRSCAN_EINVAL;
+  const uint64_t gb = G ? gw * 4 : 0;
+  if (overlap(out, ow * 4, C, cw * 4) || overlap(out, ow * 4, h_tiled, hw * 4) ||
+      overlap(out, ow * 4, G, gb))
+    return PIRSCAN_EINVAL;
+  pirscan::RowselLaunch a;
+  exppack_launch_desc(s, B, P, C, h_tiled, G, out, &a);
+  const Span ins[] = {{C, cw * 4}, {h_tiled, hw * 4}, {G, gb}, {out, ow * 4}};
+  return run_modgemm(a, s->R, ins, 4, workspace, workspace_bytes, stream);
 }
 
 size_t pirscan_scalar_workspace_bytes(uint64_t M, uint64_t K, uint32_t B) {
@@ -180,6 +337,46 @@ int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* o
   if (dc != PIRSCAN_OK) return dc;
   return device_status(
       pirscan::launch_scalar(db, query, out, M, K, B, p, workspace, (hipStream_t)stream));
+}
+
+int pirscan_kernel_timer_begin(uint32_t capacity) {
+  if (capacity == 0 || capacity > (1u << 20)) return PIRSCAN_EINVAL;
+  timer_release();
+  g_timer.start = new (std::nothrow) hipEvent_t[capacity];
+  g_timer.stop = new (std::nothrow) hipEvent_t[capacity];
+  if (!g_timer.start || !g_timer.stop) {
+    timer_release();
+    return PIRSCAN_EINVAL;
+  }
+  for (uint32_t i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&g_timer.start[i]);
+    if (e == hipSuccess) {
+      e = hipEventCreate(&g_timer.stop[i]);
+      if (e != hipSuccess) (void)hipEventDestroy(g_timer.start[i]);
+    }
+    if (e != hipSuccess) {
+      g_timer.cap = i;
+      timer_release();
+      return device_status(e);
+    }
+    g_timer.cap = i + 1;
+  }
+  g_timer.on = true;
+  return PIRSCAN_OK;
+}
+
+int pirscan_kernel_timer_end(float* ms, uint32_t max_count, uint32_t* count) {
+  if (!g_timer.on) return PIRSCAN_EINVAL;
+  const uint32_t n = g_timer.count < max_count ? g_timer.count : max_count;
+  int st = PIRSCAN_OK;
+  for (uint32_t i = 0; i < n && st == PIRSCAN_OK; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.stop[i]);
+    if (e == hipSuccess && ms) e = hipEventElapsedTime(&ms[i], g_timer.start[i], g_timer.stop[i]);
+    st = device_status(e);
+  }
+  if (count) *count = st == PIRSCAN_OK ? n : 0;
+  timer_release();
+  return st;
 }
 
 const char* pirscan_strerror(int status) {

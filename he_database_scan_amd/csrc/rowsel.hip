@@ -6,8 +6,12 @@
 //
 //     out[mi][n][p] = ( sum_k ct[mi][k][p] * db[k][n][p] ) mod q_{p/N}
 //
+// The same kernel runs VIPIR's ExpPack packing GEMM (section 3.5.2,
+// H*C + (0|G)) with the operands' roles swapped: ct = C^T, db = H^T, strided
+// ct / out addressing, and the body term G added by the output relayout.
+//
 // Design (MI355X-first, HBM-bound at small m):
-//  * The DB is static, so it is relaid once (layout_db_kernel) from the
+//  * The DB is static, so it is relaid once (transpose_kernel) from the
 //    p-major HE layout [k][n][p] to [p][k][n]: for a fixed point every k-row
 //    of D1 words is contiguous and a wavefront streams it with 128-bit loads.
 //    (GPIR moves RowSel to a transposed layout; VIPIR section 4.2 transposes
@@ -23,6 +27,10 @@
 //    more v_mad_u64_u32, keeps the value congruent mod q and bounds it so the
 //    next `fold` products cannot overflow (the bound is computed per prime on
 //    the host).  One Barrett reduction per output gives the canonical residue.
+//  * Residues are staged per point ([p][mi][n], 128-bit stores into the
+//    caller's workspace) and a tiled transpose writes the p-major output: a
+//    direct p-major store is one scattered 4-byte write per residue, which
+//    HBM serves as a partial-line write and which cost ~13% of the scan.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -35,26 +43,41 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLdsWords = 8192;  // 32 KiB of staged ct per workgroup
 
 // ---------------------------------------------------------------------------
-// R1: one-time DB relayout [X][P] -> [P][X], X = D0*D1, via 64x64 LDS tiles.
+// Batched word transposes via 64x64 LDS tiles: R1's one-time DB relayout
+// [X][P] -> [P][X], the ExpPack hint relayout, and the per-query ct / output
+// relayouts of the batched MFMA path (which fuse ExpPack's body term).
 // ---------------------------------------------------------------------------
 constexpr int kTile = 64;
 
-__global__ __launch_bounds__(kThreads) void layout_db_kernel(const uint32_t* __restrict__ src,
-                                                             uint32_t* __restrict__ dst,
-                                                             uint64_t X, uint64_t P,
-                                                             uint64_t tiles_x, uint64_t tiles) {
+template <bool kAdd>
+__global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeDesc t, uint64_t tiles_c,
+                                                             uint64_t tiles_rc, uint64_t tiles) {
   __shared__ uint32_t tile[kTile][kTile + 1];
   const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
-  for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const uint64_t x0 = (t % tiles_x) * kTile, p0 = (t / tiles_x) * kTile;
-    for (int r = ty; r < kTile; r += kThreads / kTile) {
-      const uint64_t x = x0 + r, p = p0 + tx;
-      tile[r][tx] = (x < X && p < P) ? src[x * P + p] : 0u;
+  for (uint64_t id = blockIdx.x; id < tiles; id += gridDim.x) {
+    const uint64_t b = id / tiles_rc, rc = id % tiles_rc;
+    const uint64_t c0 = (rc % tiles_c) * kTile, r0 = (rc / tiles_c) * kTile;
+    const uint32_t* src = t.src + b * t.s_batch;
+    for (int i = ty; i < kTile; i += kThreads / kTile) {
+      const uint64_t r = r0 + i, c = c0 + tx;
+      tile[i][tx] = (r < t.rows && c < t.cols) ? src[r * t.s_row + c] : 0u;
     }
     __syncthreads();
-    for (int r = ty; r < kTile; r += kThreads / kTile) {
-      const uint64_t p = p0 + r, x = x0 + tx;
-      if (p < P && x < X) dst[p * X + x] = tile[tx][r];
+    uint32_t* dst = t.dst + b * t.d_batch;
+    for (int i = ty; i < kTile; i += kThreads / kTile) {
+      const uint64_t c = c0 + i, r = r0 + tx;
+      if (c < t.cols && r < t.rows) {
+        uint32_t v = tile[tx][i];
+        if constexpr (kAdd) {
+          if (b & 1) {  // (0 | G): the body term goes to each client's second column
+            const uint64_t q = t.lc.q[r / t.N];
+            uint64_t x = (uint64_t)v + t.add[(b >> 1) * t.add_b + c * t.add_c + r];
+            if (x >= q) x -= q;
+            v = (uint32_t)x;
+          }
+        }
+        dst[c * t.d_row + r] = v;
+      }
     }
     __syncthreads();
   }
@@ -110,6 +133,42 @@ struct Vec<1, NT> {
   __device__ __forceinline__ void load(const uint32_t* p) { v[0] = ld1<NT>(p); }
 };
 
+// acc[i][j] += ct value of row i (from LDS) * DB word j of k-row kk.
+template <int MR, int RPL, int NPL, bool NT>
+__device__ __forceinline__ void mac_row(uint64_t (&acc)[RPL][NPL], const uint32_t* L, uint32_t kk,
+                                        const Vec<NPL, NT>& d) {
+  uint32_t cv[RPL];
+  if constexpr (RPL == 1) {
+    cv[0] = L[kk * MR];
+  } else if constexpr (RPL == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(L + kk * MR);
+    cv[0] = t.x;
+    cv[1] = t.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPL; i += 4) {
+      const uint4 t = *reinterpret_cast<const uint4*>(L + kk * MR + i);
+      cv[i] = t.x;
+      cv[i + 1] = t.y;
+      cv[i + 2] = t.z;
+      cv[i + 3] = t.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPL; ++i)
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) acc[i][j] += (uint64_t)cv[i] * d.v[j];
+}
+
+// fold: hi*2^32 + lo == hi*(2^32 mod q) + lo  (mod q)
+template <int RPL, int NPL>
+__device__ __forceinline__ void fold_acc(uint64_t (&acc)[RPL][NPL], uint64_t cfold) {
+#pragma unroll
+  for (int i = 0; i < RPL; ++i)
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) acc[i][j] = (acc[i][j] >> 32) * cfold + (uint32_t)acc[i][j];
+}
+
 // MR:  ct rows handled per pass (m padded up to MR with zero rows).
 // G:   row groups per wavefront.  Lane l works on rows [g*MR/G, (g+1)*MR/G)
 //      of the pass, g = l / (64/G), and on NPL columns; so each ct value read
@@ -119,7 +178,7 @@ struct Vec<1, NT> {
 //      per wavefront (LDS bandwidth, not the multiplier, would otherwise bound
 //      the scan).
 // NPL: DB columns per lane (256/128/32-bit loads).
-// UNR: k-rows whose loads are issued back to back (must divide the fold).
+// UNR: k-rows kept in flight per lane (must divide the fold period).
 template <int MR, int G, int NPL, int UNR>
 __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32_t m_base,
                                                           uint32_t nslices, uint64_t items) {
@@ -159,66 +218,55 @@ __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32
   for (uint32_t k0 = 0; k0 < a.D0; k0 += KC) {
     const uint32_t kc = (a.D0 - k0) < (uint32_t)KC ? (a.D0 - k0) : (uint32_t)KC;
     __syncthreads();  // the previous chunk is fully consumed
-    // Stage ct[m_base+mi][k0+kk][p_lo+pt] -> lds[(pt*KC + kk)*MR + mi]; the
+    // Stage ct(m_base+mi, k0+kk, p_lo+pt) -> lds[(pt*KC + kk)*MR + mi]; the
     // point index is fastest so global reads are runs along p.
     const uint32_t total = npts * kc * MR;
     for (uint32_t e = threadIdx.x; e < total; e += kThreads) {
       const uint32_t pt = e % npts, rest = e / npts;
       const uint32_t mi = rest % MR, kk = rest / MR;
       uint32_t v = 0;
-      if (mi < mrows) v = a.ct[((uint64_t)(m_base + mi) * a.D0 + k0 + kk) * a.P + p_lo + pt];
+      if (mi < mrows) v = a.ct[(uint64_t)(m_base + mi) * a.ct_sm + (uint64_t)(k0 + kk) * a.ct_sk + p_lo + pt];
       lds[(pt * KC + kk) * MR + mi] = v;
     }
     __syncthreads();
     if (lane_on) {
       const uint32_t* L = lds + pl * (KC * MR) + grp * RPL;
-      for (uint32_t s0 = 0; s0 < kc; s0 += a.fold) {
-        const uint32_t s1 = (s0 + a.fold < kc) ? s0 + a.fold : kc;
-        uint32_t kk = s0;
-        if constexpr (UNR > 1) {
-          for (; kk + UNR <= s1; kk += UNR) {
-            Vec<NPL, NT> d[UNR];
+      const uint32_t* rowp = dbp + (uint64_t)k0 * a.D1;
+      const uint32_t fmask = a.fold - 1;  // the fold period is a power of two
+      uint32_t kk = 0;
+      if constexpr (UNR > 1) {
+        // A rolling ring of UNR rows: slot u is refilled with the row UNR
+        // ahead as soon as it has been consumed, so UNR row loads stay in
+        // flight while the products run.  UNR divides the fold period, so
+        // every fold falls on a group boundary.
+        if (kc >= (uint32_t)UNR) {
+          Vec<NPL, NT> d[UNR];
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) d[u].load(dbp + (uint64_t)(k0 + kk + u) * a.D1);
+          for (int u = 0; u < UNR; ++u) d[u].load(rowp + (uint64_t)u * a.D1);
+          for (; kk + 2 * UNR <= kc; kk += UNR) {
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-              uint32_t cv[RPL];
-              if constexpr (RPL == 1) {
-                cv[0] = L[(kk + u) * MR];
-              } else if constexpr (RPL == 2) {
-                const uint2 t = *reinterpret_cast<const uint2*>(L + (kk + u) * MR);
-                cv[0] = t.x; cv[1] = t.y;
-              } else {
-#pragma unroll
-                for (int i = 0; i < RPL; i += 4) {
-                  const uint4 t = *reinterpret_cast<const uint4*>(L + (kk + u) * MR + i);
-                  cv[i] = t.x; cv[i + 1] = t.y; cv[i + 2] = t.z; cv[i + 3] = t.w;
-                }
-              }
-#pragma unroll
-              for (int i = 0; i < RPL; ++i)
-#pragma unroll
-                for (int j = 0; j < NPL; ++j) acc[i][j] += (uint64_t)cv[i] * d[u].v[j];
+              mac_row<MR, RPL, NPL, NT>(acc, L, kk + u, d[u]);
+              d[u].load(rowp + (uint64_t)(kk + UNR + u) * a.D1);
+              // keep the refills in slot order: loads complete in issue order,
+              // so the next slot then waits only for its own row
+              __builtin_amdgcn_sched_barrier(0);
             }
+            if (((kk + UNR) & fmask) == 0) fold_acc(acc, cfold);
           }
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) mac_row<MR, RPL, NPL, NT>(acc, L, kk + u, d[u]);
+          kk += UNR;
+          if ((kk & fmask) == 0) fold_acc(acc, cfold);
         }
-        for (; kk < s1; ++kk) {
-          Vec<NPL, NT> d;
-          d.load(dbp + (uint64_t)(k0 + kk) * a.D1);
-#pragma unroll
-          for (int i = 0; i < RPL; ++i) {
-            const uint64_t cvi = L[kk * MR + i];
-#pragma unroll
-            for (int j = 0; j < NPL; ++j) acc[i][j] += cvi * d.v[j];
-          }
-        }
-        // fold: hi*2^32 + lo == hi*(2^32 mod q) + lo  (mod q)
-#pragma unroll
-        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-          for (int j = 0; j < NPL; ++j)
-            acc[i][j] = (acc[i][j] >> 32) * cfold + (uint32_t)acc[i][j];
       }
+      for (; kk < kc; ++kk) {
+        Vec<NPL, NT> d;
+        d.load(rowp + (uint64_t)kk * a.D1);
+        mac_row<MR, RPL, NPL, NT>(acc, L, kk, d);
+        if (((kk + 1) & fmask) == 0) fold_acc(acc, cfold);
+      }
+      fold_acc(acc, cfold);  // bounded again for the next chunk and the reduction
     }
   }
 
@@ -227,15 +275,29 @@ __global__ __launch_bounds__(kThreads) void rowsel_kernel(RowselLaunch a, uint32
     const uint64_t mu = a.lc.mu[limb];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const uint32_t mi = grp * RPL + i;
-      if (mi < mrows) {
+      const uint32_t mi = m_base + grp * RPL + i;
+      if (grp * RPL + i < mrows) {
+        uint32_t r[NPL];
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-          // Barrett with mu = floor((2^64-1)/q): the estimate is at most one short.
+          // Barrett with mu = floor((2^64-1)/q): the estimate is at most one
+          // short of the quotient.
           const uint64_t x = acc[i][j];
-          uint64_t r = x - __umul64hi(x, mu) * q;
-          if (r >= q) r -= q;
-          a.out[((uint64_t)(m_base + mi) * a.D1 + n0 + j) * a.P + p] = (uint32_t)r;
+          uint64_t t = x - __umul64hi(x, mu) * q;
+          if (t >= q) t -= q;
+          r[j] = (uint32_t)t;
+        }
+        // Per-point staging: the lane's NPL columns are contiguous, so the
+        // store is one 128-bit write per 4 columns (a p-major store would be
+        // a scattered 4-byte write per residue).
+        uint32_t* dst = a.out_t + ((uint64_t)p * a.m + mi) * a.D1 + n0;
+        if constexpr (NPL % 4 == 0) {
+#pragma unroll
+          for (int j = 0; j < NPL; j += 4)
+            *reinterpret_cast<uint4*>(dst + j) = make_uint4(r[j], r[j + 1], r[j + 2], r[j + 3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NPL; ++j) dst[j] = r[j];
         }
       }
     }
@@ -287,17 +349,60 @@ uint32_t rowsel_fold_period(uint32_t q) {
   return p2;  // >= 1 for every 2 <= q < 2^32
 }
 
-hipError_t launch_layout_db(const uint32_t* src, uint32_t* dst, uint64_t X, uint64_t P,
-                            hipStream_t stream) {
-  const uint64_t tiles_x = (X + kTile - 1) / kTile, tiles_p = (P + kTile - 1) / kTile;
-  const uint64_t tiles = tiles_x * tiles_p;
+hipError_t launch_transpose(const TransposeDesc& t, hipStream_t stream) {
+  if (t.batch == 0 || t.rows == 0 || t.cols == 0) return hipSuccess;
+  const uint64_t tiles_c = (t.cols + kTile - 1) / kTile, tiles_r = (t.rows + kTile - 1) / kTile;
+  const uint64_t tiles_rc = tiles_c * tiles_r, tiles = tiles_rc * t.batch;
   const uint64_t grid = tiles < (1ull << 20) ? tiles : (1ull << 20);
-  hipLaunchKernelGGL(layout_db_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, src, dst, X,
-                     P, tiles_x, tiles);
+  if (t.add)
+    hipLaunchKernelGGL(transpose_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, t,
+                       tiles_c, tiles_rc, tiles);
+  else
+    hipLaunchKernelGGL(transpose_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, t,
+                       tiles_c, tiles_rc, tiles);
   return hipGetLastError();
 }
 
-hipError_t launch_rowsel(const RowselLaunch& a, hipStream_t stream) {
+hipError_t launch_layout_db(const uint32_t* src, uint32_t* dst, uint64_t X, uint64_t P,
+                            hipStream_t stream) {
+  TransposeDesc t{};
+  t.src = src;
+  t.dst = dst;
+  t.batch = 1;
+  t.rows = X;
+  t.cols = P;
+  t.s_row = P;
+  t.d_row = X;
+  return launch_transpose(t, stream);
+}
+
+size_t rowsel_valu_workspace_bytes(uint64_t P, uint32_t m, uint32_t D1) {
+  return (size_t)((4ull * P * m * D1 + 255) / 256 * 256);
+}
+
+hipError_t launch_out_relayout(const RowselLaunch& a, const uint32_t* out_t, hipStream_t stream) {
+  TransposeDesc to{};
+  to.src = out_t;
+  to.dst = a.out;
+  to.batch = a.m;
+  to.rows = a.P;
+  to.cols = a.D1;
+  to.s_batch = a.D1;
+  to.s_row = (uint64_t)a.m * a.D1;
+  to.d_batch = a.out_sm;
+  to.d_row = a.out_sn;
+  to.add = a.add;
+  to.add_b = a.add_sb;
+  to.add_c = a.add_sn;
+  to.N = a.N;
+  to.lc = a.lc;
+  return launch_transpose(to, stream);
+}
+
+hipError_t launch_rowsel(const RowselLaunch& a0, void* workspace, hipStream_t stream) {
+  RowselLaunch a = a0;
+  a.out_t = static_cast<uint32_t*>(workspace);
+  timer_mark_start(stream);
   for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
     const uint32_t rows = a.m - m_base;
     hipError_t e;
@@ -308,7 +413,8 @@ hipError_t launch_rowsel(const RowselLaunch& a, hipStream_t stream) {
     else e = launch_mr<32, 2, 4>(a, m_base, stream);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  timer_mark_stop(stream);
+  return launch_out_relayout(a, a.out_t, stream);
 }
 
 }  // namespace pirscan

@@ -24,7 +24,8 @@
 //
 // Data movement:
 //  * ct is relaid per query (two small passes into the caller's workspace):
-//    a transpose to [p][mi][k] and a limb split into MFMA A-fragment order, so
+//    a strided transpose to [p][mi][k] (from RowSel's [mi][k][p] or ExpPack's
+//    C [k][mi][p]) and a limb split into MFMA A-fragment order, so
 //    each wavefront loads its A fragments as 16-byte vectors.
 //  * The DB stays in the scan layout [p][k][n].  Lane (li, lg) of a B fragment
 //    needs 16 consecutive k of column n0+li; it loads them as 16 dwords (each
@@ -32,7 +33,8 @@
 //    four limb fragments in registers.  Two column tiles are interleaved so each
 //    128-byte row line is read by back-to-back requests.
 //  * Results are written per point, [p][mi][n] (contiguous 64-byte runs), and
-//    a transpose pass produces the p-major [mi][n][p] output.
+//    a transpose pass produces the p-major output (adding ExpPack's body term
+//    G where the launch carries one).
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -272,8 +274,18 @@ hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace
     ep.corr[r] = (uint32_t)((q - off) % q);
   }
 
-  // ct [m*D0][P] -> ct_t [P][m*D0]
-  hipError_t e = launch_layout_db(a.ct, ct_t, (uint64_t)a.m * a.D0, a.P, stream);
+  // ct(mi, k, p) -> ct_t [P][m][D0]
+  TransposeDesc tc{};
+  tc.src = a.ct;
+  tc.dst = ct_t;
+  tc.batch = a.m;
+  tc.rows = a.D0;
+  tc.cols = a.P;
+  tc.s_batch = a.ct_sm;
+  tc.s_row = a.ct_sk;
+  tc.d_batch = a.D0;
+  tc.d_row = (uint64_t)a.m * a.D0;
+  hipError_t e = launch_transpose(tc, stream);
   if (e != hipSuccess) return e;
   for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
     const uint32_t rows = a.m - m_base;
@@ -281,12 +293,14 @@ hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace
     hipLaunchKernelGGL(rowsel_limbs_kernel, dim3(grid_for(a.P * S * MT * 64)), dim3(kThreads), 0, stream,
                        ct_t, limbs, a.P, a.m, a.D0, m_base, MT, S, a.N, a.lc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark_start(stream);  // first pass only
     if (MT == 2) e = launch_mfma_pass<2, 2>(a, ep, limbs, out_t, m_base, S, stream);
     else e = launch_mfma_pass<1, 2>(a, ep, limbs, out_t, m_base, S, stream);
     if (e != hipSuccess) return e;
   }
-  // out_t [P][m*D1] -> out [m*D1][P]
-  return launch_layout_db(out_t, a.out, a.P, (uint64_t)a.m * a.D1, stream);
+  timer_mark_stop(stream);
+  // out_t [P][m][D1] -> out(mi, n, p), adding ExpPack's body term on the way
+  return launch_out_relayout(a, out_t, stream);
 }
 
 }  // namespace pirscan

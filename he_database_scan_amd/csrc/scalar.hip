@@ -507,8 +507,10 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
                          uint64_t K, uint32_t B, const ScalarPlan& pl, void* workspace,
                          hipStream_t stream) {
   if (!pl.fast) {
+    timer_mark_start(stream);
     hipLaunchKernelGGL(generic_kernel, dim3(grid_for(M * B)), dim3(kThreads), 0, stream, db, query,
                        out, M, K, B);
+    timer_mark_stop(stream);
     return hipGetLastError();
   }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -524,8 +526,10 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
     const uint64_t grid = row_blocks * pl.nkb;
     if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
     uint32_t* dst = pl.nkb > 1 ? part : out;
+    timer_mark_start(stream);
     hipLaunchKernelGGL(gemv_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, db, dig, dst, M,
                        K, pl.nkb);
+    timer_mark_stop(stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (pl.nkb > 1) {
       hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M)), dim3(kThreads), 0, stream, part, out, M, 1u,
@@ -543,6 +547,7 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
                        dig, K, k16, bpad, bg, B, c0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint32_t* dst = pl.nkb > 1 ? part : out;
+    timer_mark_start(stream);  // first pass only
     if (bpad == 16) e = launch_mfma<4>(db, dig, dst, M, K, pl, bg, B, c0, stream);
     else e = launch_mfma<8>(db, dig, dst, M, K, pl, bg, B, c0, stream);
     if (e != hipSuccess) return e;
@@ -552,6 +557,7 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
+  timer_mark_stop(stream);
   return hipSuccess;
 }
 

@@ -42,6 +42,29 @@ class RowselShape(ctypes.Structure):
         return self.N * self.R
 
 
+class ExppackShape(ctypes.Structure):
+    """pirscan_exppack_shape: N points per limb, R limbs with moduli q, Dr output
+    ciphertexts (rows of H and G), n LWE dimension (columns of H, rows of C)."""
+
+    _fields_ = [("N", ctypes.c_uint32), ("R", ctypes.c_uint32), ("q", ctypes.c_uint32 * MAX_R),
+                ("Dr", ctypes.c_uint32), ("n", ctypes.c_uint32)]
+
+    @classmethod
+    def make(cls, N: int, q, Dr: int, n: int) -> "ExppackShape":
+        q = [int(v) for v in q]
+        if not 1 <= len(q) <= MAX_R:
+            raise ValueError(f"need 1..{MAX_R} moduli")
+        s = cls()
+        s.N, s.R, s.Dr, s.n = N, len(q), Dr, n
+        for i, v in enumerate(q):
+            s.q[i] = v
+        return s
+
+    @property
+    def P(self) -> int:
+        return self.N * self.R
+
+
 class PirscanError(RuntimeError):
     def __init__(self, fn: str, status: int):
         lib = _load()
@@ -71,10 +94,23 @@ def _load():
         L.pirscan_rowsel_workspace_bytes.restype = sz
         L.pirscan_rowsel_modgemm.argtypes = [shp, u32, vp, vp, vp, vp, sz, vp]
         L.pirscan_rowsel_modgemm.restype = ctypes.c_int
+        ehp = ctypes.POINTER(ExppackShape)
+        L.pirscan_exppack_layout_h_bytes.argtypes = [ehp]
+        L.pirscan_exppack_layout_h_bytes.restype = sz
+        L.pirscan_exppack_layout_h.argtypes = [ehp, vp, vp, vp]
+        L.pirscan_exppack_layout_h.restype = ctypes.c_int
+        L.pirscan_exppack_workspace_bytes.argtypes = [ehp, u32]
+        L.pirscan_exppack_workspace_bytes.restype = sz
+        L.pirscan_exppack_modgemm.argtypes = [ehp, u32, vp, vp, vp, vp, vp, sz, vp]
+        L.pirscan_exppack_modgemm.restype = ctypes.c_int
         L.pirscan_scalar_workspace_bytes.argtypes = [u64, u64, u32]
         L.pirscan_scalar_workspace_bytes.restype = sz
         L.pirscan_scalar_gemm_u32.argtypes = [vp, vp, vp, u64, u64, u32, vp, sz, vp]
         L.pirscan_scalar_gemm_u32.restype = ctypes.c_int
+        L.pirscan_kernel_timer_begin.argtypes = [u32]
+        L.pirscan_kernel_timer_begin.restype = ctypes.c_int
+        L.pirscan_kernel_timer_end.argtypes = [ctypes.POINTER(ctypes.c_float), u32, ctypes.POINTER(u32)]
+        L.pirscan_kernel_timer_end.restype = ctypes.c_int
         L.pirscan_strerror.argtypes = [ctypes.c_int]
         L.pirscan_strerror.restype = ctypes.c_char_p
         L.pirscan_version.argtypes = []
@@ -150,7 +186,7 @@ def rowsel_modgemm(shape: RowselShape, m: int, ct, db_tiled, out, workspace=None
     """out[m][D1][P] = RowSel(ct[m][D0][P], db) mod q, on device.
 
     ``workspace``: a device buffer of at least ``rowsel_workspace_bytes(shape, m)``
-    bytes (any dtype; may be None when that size is 0), owned by the caller.
+    bytes (any dtype), owned by the caller.
     """
     P = shape.P
     _dev(ct, "ct", 4, m * shape.D0 * P)
@@ -160,6 +196,43 @@ def rowsel_modgemm(shape: RowselShape, m: int, ct, db_tiled, out, workspace=None
     _check("pirscan_rowsel_modgemm",
            _load().pirscan_rowsel_modgemm(ctypes.byref(shape), m, _ptr(ct), _ptr(db_tiled), _ptr(out),
                                           _ptr(workspace), wbytes, _stream(stream)))
+
+
+def exppack_layout_h_bytes(shape: ExppackShape) -> int:
+    return int(_load().pirscan_exppack_layout_h_bytes(ctypes.byref(shape)))
+
+
+def exppack_layout_h(shape: ExppackShape, h_pmajor, h_tiled, stream=None) -> None:
+    """h_pmajor [Dr][n][P] (uint32 bits) -> h_tiled (same word count)."""
+    n = shape.Dr * shape.n * shape.P
+    _dev(h_pmajor, "h_pmajor", 4, n)
+    _dev(h_tiled, "h_tiled", 4, n)
+    _check("pirscan_exppack_layout_h",
+           _load().pirscan_exppack_layout_h(ctypes.byref(shape), _ptr(h_pmajor), _ptr(h_tiled),
+                                            _stream(stream)))
+
+
+def exppack_workspace_bytes(shape: ExppackShape, B: int) -> int:
+    return int(_load().pirscan_exppack_workspace_bytes(ctypes.byref(shape), B))
+
+
+def exppack_modgemm(shape: ExppackShape, B: int, C, h_tiled, G, out, workspace=None, stream=None) -> None:
+    """out[Dr][2B][P] = H*C + (0|G) mod q, on device (VIPIR section 3.5.2).
+
+    C [n][2B][P], G [Dr][B][P] or None, all uint32 bits in 4-byte tensors.
+    ``workspace``: at least ``exppack_workspace_bytes(shape, B)`` bytes, owned
+    by the caller.
+    """
+    P = shape.P
+    _dev(C, "C", 4, shape.n * 2 * B * P)
+    _dev(h_tiled, "h_tiled", 4, shape.Dr * shape.n * P)
+    if G is not None:
+        _dev(G, "G", 4, shape.Dr * B * P)
+    _dev(out, "out", 4, shape.Dr * 2 * B * P)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pirscan_exppack_modgemm",
+           _load().pirscan_exppack_modgemm(ctypes.byref(shape), B, _ptr(C), _ptr(h_tiled), _ptr(G),
+                                           _ptr(out), _ptr(workspace), wbytes, _stream(stream)))
 
 
 def scalar_workspace_bytes(M: int, K: int, B: int) -> int:
@@ -183,3 +256,17 @@ def scalar_gemm_u32(db, query, out, workspace=None, stream=None) -> None:
            _load().pirscan_scalar_gemm_u32(_ptr(db), _ptr(query), _ptr(out), M, K, B,
                                            _ptr(workspace) if need else ctypes.c_void_p(0),
                                            wbytes, _stream(stream)))
+
+
+def kernel_timer_begin(capacity: int) -> None:
+    """Benchmark hook: time the main kernel of the next ``capacity`` scan calls
+    of this thread with HIP events on their stream."""
+    _check("pirscan_kernel_timer_begin", _load().pirscan_kernel_timer_begin(capacity))
+
+
+def kernel_timer_end(max_count: int) -> list:
+    """Waits for the recorded events; returns each call's main-kernel time (ms)."""
+    buf = (ctypes.c_float * max(1, max_count))()
+    n = ctypes.c_uint32(0)
+    _check("pirscan_kernel_timer_end", _load().pirscan_kernel_timer_end(buf, max_count, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]

@@ -12,6 +12,12 @@
  *
  *      out[mi][n][p] = ( sum_{k<D0} ct[mi][k][p] * db[k][n][p] ) mod q[p / N]
  *
+ *  ExpPack packing GEMM (VIPIR section 3.5.2: H*C + (0|G) after the NTT is a
+ *  (#RNS*N)-parallel ceil(D1/N) x 2B x n INT32 GEMM with modular reduction):
+ *
+ *      out[r][j][p] = ( sum_{i<n} H[r][i][p] * C[i][j][p] + Z[r][j][p] ) mod q[p / N]
+ *      Z[r][2b+1][p] = G[r][b][p],  Z[r][2b][p] = 0
+ *
  *  Scalar-HE / Regev (VIPIR section 2.5, the D1 x B x D0 INT8-INT32 GEMM of
  *  batched SimplePIR; VIPIR section 4, where reduction mod 2^32 is free):
  *
@@ -41,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PIRSCAN_VERSION 10000 /* 1.0.0 */
+#define PIRSCAN_VERSION 10100 /* 1.1.0 */
 #define PIRSCAN_MAX_R 8
 
 enum {
@@ -88,11 +94,11 @@ int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor,
                       uint32_t* db_tiled, void* stream);
 
 /*
- * Workspace bytes pirscan_rowsel_modgemm needs for (shape, m): 0 when the
- * batch runs on the VALU path (m < 16, a modulus >= 2^31, or D0 > 16384),
- * else room for the per-query relayout of ct and of the output used by the
- * int8-MFMA path (GPIR: batching makes RowSel a dense contraction).  0 also
- * on an invalid shape.
+ * Workspace bytes pirscan_rowsel_modgemm needs for (shape, m): room for the
+ * per-point staging of the output (4 * P * m * D1 bytes, rounded up to 256),
+ * and, when the batch runs on int8 MFMA (m >= 16, every modulus < 2^31,
+ * D0 <= 16384; GPIR: batching makes RowSel a dense contraction), for the
+ * per-query relayout of ct as well.  0 only on an invalid shape or m == 0.
  */
 size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m);
 
@@ -104,9 +110,8 @@ size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m)
  *   db_tiled  : output of pirscan_layout_db for the same shape.
  *   out       : [m][D1][P] uint32, p-major, canonical residues in [0, q[p/N]).
  *   workspace : >= pirscan_rowsel_workspace_bytes(s, m) bytes of device
- *               memory, 16-byte aligned, owned by the caller (may be NULL with
- *               workspace_bytes 0 when that size is 0); contents ignored on
- *               entry and unspecified on return.
+ *               memory, 16-byte aligned, owned by the caller; contents ignored
+ *               on entry and unspecified on return.
  * Entries >= q are a precondition violation (not checked; the result is then
  * unspecified but memory-safe).  `out` and `workspace` must not overlap ct,
  * db_tiled or each other.
@@ -115,6 +120,67 @@ int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m,
                            const uint32_t* ct, const uint32_t* db_tiled,
                            uint32_t* out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * Shape of one ExpPack packing GEMM (VIPIR section 3.5.2; section 3.6 sizes it
+ * at N = 2^12, #RNS = 3, Dr = 2^8, n = 1280).  P = R*N points as for RowSel.
+ * Read by value during the call.
+ */
+typedef struct {
+  uint32_t N;                  /* points per RNS limb (polynomial degree) */
+  uint32_t R;                  /* RNS limbs, 1..PIRSCAN_MAX_R */
+  uint32_t q[PIRSCAN_MAX_R];   /* moduli, each in [2, 2^32); q[r] for r >= R ignored */
+  uint32_t Dr;                 /* output ciphertexts, ceil(D1 / N): rows of H and G */
+  uint32_t n;                  /* LWE dimension: columns of H, rows of C */
+} pirscan_exppack_shape;
+
+/* Bytes of the tiled hint produced by pirscan_exppack_layout_h: exactly
+ * 4 * P * Dr * n.  0 if the shape is invalid. */
+size_t pirscan_exppack_layout_h_bytes(const pirscan_exppack_shape* s);
+
+/*
+ * One-time relayout of the NTT-domain hint H (VIPIR section 3.6: H is
+ * computed offline and is, after the database, the largest object the
+ * packing streams; section 4.2 transposes between the polynomial-major NTT
+ * layout and the GEMM layout).
+ *   h_pmajor : [Dr][n][P] uint32, p-major, entries < q[p / N].
+ *   h_tiled  : pirscan_exppack_layout_h_bytes(s) bytes, opaque layout consumed
+ *              by pirscan_exppack_modgemm.
+ * Must not overlap.  Pure permutation of words.
+ */
+int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_pmajor,
+                             uint32_t* h_tiled, void* stream);
+
+/*
+ * Workspace bytes pirscan_exppack_modgemm needs for (shape, B): room for the
+ * per-point staging of the output (4 * P * 2B * Dr bytes, rounded up to 256)
+ * and, when the batch runs on int8 MFMA (2B >= 16, every modulus < 2^31,
+ * n <= 16384), for the per-query relayout of C.  0 only on an invalid shape
+ * or B == 0.
+ */
+size_t pirscan_exppack_workspace_bytes(const pirscan_exppack_shape* s, uint32_t B);
+
+/*
+ * ExpPack packing GEMM for B clients:
+ *   out[r][j][p] = (sum_i H[r][i][p] * C[i][j][p] + Z[r][j][p]) mod q[p/N],
+ *   Z[r][2b+1][p] = G[r][b][p], Z[r][2b][p] = 0.
+ *   B         : clients, >= 1; client b owns columns 2b and 2b+1 of C and out
+ *               (the two polynomials of its ciphertexts).
+ *   C         : [n][2B][P] uint32, p-major, entries < q[p/N]: the expanded
+ *               special ciphertexts (n x 2B matrix of polynomials).
+ *   h_tiled   : output of pirscan_exppack_layout_h for the same shape.
+ *   G         : [Dr][B][P] uint32, p-major, entries < q[p/N] (the NTT of the
+ *               first-step outputs), or NULL for G = 0.
+ *   out       : [Dr][2B][P] uint32, p-major, canonical residues in [0, q[p/N]):
+ *               Dr packed ciphertexts per client.
+ *   workspace : >= pirscan_exppack_workspace_bytes(s, B) bytes, 16-byte
+ *               aligned, caller-owned; contents ignored on entry.
+ * Entries >= q are a precondition violation (unchecked; memory-safe).  `out`
+ * and `workspace` must not overlap C, h_tiled, G or each other.
+ */
+int pirscan_exppack_modgemm(const pirscan_exppack_shape* s, uint32_t B, const uint32_t* C,
+                            const uint32_t* h_tiled, const uint32_t* G, uint32_t* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes pirscan_scalar_gemm_u32 needs for (M, K, B): the signed
  * digit planes of the query plus split-K partial sums.  0 on invalid sizes. */
@@ -138,6 +204,22 @@ size_t pirscan_scalar_workspace_bytes(uint64_t M, uint64_t K, uint32_t B);
 int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* out,
                             uint64_t M, uint64_t K, uint32_t B,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Benchmark hook for the calling thread (not part of the scan).
+ * pirscan_kernel_timer_begin(capacity) makes the thread's next `capacity`
+ * scan calls record a pair of HIP events on their stream around their main
+ * kernel -- the scan kernel itself, without the per-query pre- and
+ * post-passes (digit split, ct / output relayout, split-K reduction); the
+ * passes of a batch wider than one kernel launch are timed as one interval.
+ * pirscan_kernel_timer_end waits for the recorded events, writes the elapsed
+ * milliseconds of each call, in call order, to the HOST array ms[0..*count)
+ * (at most max_count entries) and turns the hook off.  The events belong to
+ * the library.  Not for use under stream capture.  Returns PIRSCAN_EINVAL for
+ * capacity 0 or > 2^20, or for _end without _begin.
+ */
+int pirscan_kernel_timer_begin(uint32_t capacity);
+int pirscan_kernel_timer_end(float* ms, uint32_t max_count, uint32_t* count);
 
 /* Human-readable text for a status code (static storage). */
 const char* pirscan_strerror(int status);

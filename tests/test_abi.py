@@ -24,6 +24,9 @@ def test_header_declares_the_boundary():
     for want in ("pirscan_layout_db", "pirscan_rowsel_modgemm", "pirscan_rowsel_workspace_bytes",
                  "pirscan_scalar_gemm_u32",
                  "pirscan_scalar_workspace_bytes", "pirscan_layout_db_bytes", "pirscan_strerror",
+                 "pirscan_exppack_layout_h", "pirscan_exppack_layout_h_bytes",
+                 "pirscan_exppack_workspace_bytes", "pirscan_exppack_modgemm",
+                 "pirscan_kernel_timer_begin", "pirscan_kernel_timer_end",
                  "pirscan_version", "pirscan_last_device_error"):
         assert want in names
 
@@ -35,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert pirscan.version() == 10000
+    assert pirscan.version() == 10100
     assert pirscan.strerror(0) == "ok"
     assert "invalid" in pirscan.strerror(-1)
     assert "gfx950" in pirscan.strerror(-3)
@@ -78,15 +81,17 @@ def test_page_size_identities():
 
 def test_rowsel_workspace_sizes():
     s = pirscan.RowselShape.make(4096, Q3, 1024, 1024)
-    assert pirscan.rowsel_workspace_bytes(s, 2) == 0            # VALU path, no workspace
-    assert pirscan.rowsel_workspace_bytes(s, 15) == 0
     P = 12288
+    assert pirscan.rowsel_workspace_bytes(s, 2) == 4 * P * 2 * 1024    # VALU: output staging only
+    assert pirscan.rowsel_workspace_bytes(s, 15) == 4 * P * 15 * 1024
     ct = out = 4 * P * 32 * 1024
     limbs = P * 16 * 2 * 4 * 64 * 16                            # 16 k-steps, 2 row tiles, 4 limbs
     assert pirscan.rowsel_workspace_bytes(s, 32) == ct + limbs + out
     big_q = pirscan.RowselShape.make(16, [2147483659], 64, 64)  # a modulus >= 2^31: VALU path
-    assert pirscan.rowsel_workspace_bytes(big_q, 32) == 0
-    assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(16, Q3, 20000, 64), 32) == 0
+    assert pirscan.rowsel_workspace_bytes(big_q, 32) == 4 * 16 * 32 * 64
+    assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(16, Q3, 20000, 64), 32) == 4 * 48 * 32 * 64
+    assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(1, [7], 1, 1), 1) == 256   # rounded up
+    assert pirscan.rowsel_workspace_bytes(s, 0) == 0
 
 
 def test_scalar_workspace_sizes():
@@ -108,7 +113,10 @@ def _call_rowsel(shape, m, ct, db, out, ws=0, ws_bytes=0):
 
 def test_rowsel_rejects_bad_arguments_without_a_device():
     s = pirscan.RowselShape.make(8, Q3, 4, 4)
-    A, B, C = 1 << 20, 1 << 30, 1 << 40  # fake, never dereferenced
+    A, B, C, W = 1 << 20, 1 << 30, 1 << 40, 1 << 44  # fake, never dereferenced
+    assert _call_rowsel(s, 2, A, B, C) == pirscan.EINVAL                         # no workspace
+    small = pirscan.rowsel_workspace_bytes(s, 2)
+    assert _call_rowsel(s, 2, A, B, C, W, small - 1) == pirscan.EINVAL
     assert _call_rowsel(None, 2, A, B, C) == pirscan.EINVAL
     assert _call_rowsel(s, 0, A, B, C) == pirscan.EINVAL
     assert _call_rowsel(s, 2, 0, B, C) == pirscan.EINVAL
@@ -129,6 +137,50 @@ def test_rowsel_rejects_bad_arguments_without_a_device():
     assert _call_rowsel(big, 32, A, B, C, C + 64, need) == pirscan.EINVAL       # overlaps out
     L = pirscan.lib()
     assert L.pirscan_layout_db(ctypes.byref(s), ctypes.c_void_p(A), ctypes.c_void_p(A + 16), None) == pirscan.EINVAL
+
+
+def test_exppack_sizes():
+    # VIPIR section 3.6: N = 2^12, #RNS = 3, Dr = 2^8, n = 1280 -> H is 15 GiB
+    s = pirscan.ExppackShape.make(4096, Q3, 256, 1280)
+    assert pirscan.exppack_layout_h_bytes(s) == 15 * (1 << 30)
+    P = 12288
+    assert pirscan.exppack_workspace_bytes(s, 1) == 4 * P * 2 * 256     # m = 2: VALU, output staging
+    assert pirscan.exppack_workspace_bytes(s, 7) == 4 * P * 14 * 256    # m = 14
+    ct, out = 4 * P * 32 * 1280, 4 * P * 32 * 256
+    limbs = P * 20 * 2 * 4 * 64 * 16                              # 20 k-steps of 64, 2 row tiles
+    assert pirscan.exppack_workspace_bytes(s, 16) == ct + limbs + out
+    assert pirscan.exppack_workspace_bytes(s, 0) == 0
+    for bad in (pirscan.ExppackShape.make(0, Q3, 4, 4), pirscan.ExppackShape.make(4, Q3, 0, 4),
+                pirscan.ExppackShape.make(4, Q3, 4, 0), pirscan.ExppackShape.make(4, [1], 4, 4)):
+        assert pirscan.exppack_layout_h_bytes(bad) == 0
+        assert pirscan.exppack_workspace_bytes(bad, 16) == 0
+
+
+def test_exppack_rejects_bad_arguments_without_a_device():
+    L = pirscan.lib()
+    A, H, G, O, W = 1 << 20, 1 << 30, 1 << 36, 1 << 40, 1 << 44
+    f = lambda shp, B, c, h, g, o, w=0, wb=0: L.pirscan_exppack_modgemm(
+        ctypes.byref(shp) if shp is not None else None, B, ctypes.c_void_p(c), ctypes.c_void_p(h),
+        ctypes.c_void_p(g), ctypes.c_void_p(o), ctypes.c_void_p(w), wb, None)
+    s = pirscan.ExppackShape.make(8, Q3, 4, 40)
+    assert f(None, 1, A, H, G, O) == pirscan.EINVAL
+    assert f(s, 0, A, H, G, O) == pirscan.EINVAL
+    assert f(s, 1, 0, H, G, O) == pirscan.EINVAL
+    assert f(s, 1, A, 0, G, O) == pirscan.EINVAL
+    assert f(s, 1, A, H, G, 0) == pirscan.EINVAL
+    assert f(s, 1, A, H, G, A + 4) == pirscan.EINVAL            # out overlaps C
+    assert f(s, 1, A, H, G, H + 64) == pirscan.EINVAL           # out overlaps H
+    assert f(s, 1, A, H, G, G + 8) == pirscan.EINVAL            # out overlaps G
+    need = pirscan.exppack_workspace_bytes(s, 8)
+    assert need > 0
+    assert f(s, 1, A, H, G, O) == pirscan.EINVAL                # every path needs a workspace
+    assert f(s, 8, A, H, G, O) == pirscan.EINVAL
+    assert f(s, 8, A, H, G, O, W, need - 1) == pirscan.EINVAL
+    assert f(s, 8, A, H, G, O, W + 4, need) == pirscan.EINVAL   # misaligned
+    assert f(s, 8, A, H, G, O, G, need) == pirscan.EINVAL       # workspace overlaps G
+    assert f(s, 1 << 31, A, H, G, O) == pirscan.EINVAL          # 2B overflows
+    assert L.pirscan_exppack_layout_h(ctypes.byref(s), ctypes.c_void_p(A), ctypes.c_void_p(A + 16),
+                                      None) == pirscan.EINVAL
 
 
 def test_scalar_rejects_bad_arguments_without_a_device():
@@ -153,3 +205,11 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(pirscan, "_lib", None)
     with pytest.raises(RuntimeError):
         pirscan.version()
+
+
+def test_kernel_timer_argument_checks():
+    L = pirscan.lib()
+    assert L.pirscan_kernel_timer_begin(0) == pirscan.EINVAL
+    assert L.pirscan_kernel_timer_begin((1 << 20) + 1) == pirscan.EINVAL
+    n = ctypes.c_uint32(7)
+    assert L.pirscan_kernel_timer_end(None, 0, ctypes.byref(n)) == pirscan.EINVAL   # not begun
