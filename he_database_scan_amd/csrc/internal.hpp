@@ -75,7 +75,7 @@ hipError_t launch_rowsel(const RowselLaunch& a, void* workspace, hipStream_t str
 hipError_t launch_out_relayout(const RowselLaunch& a, const uint32_t* out_t, hipStream_t stream);
 
 // Batched RowSel on int8 MFMA: m >= kRowselMfmaMinRows, every q < 2^31,
-// D0 <= 16384.  Needs a workspace of rowsel_mfma_workspace_bytes().
+// D0 <= 16384, D0*D1 < 2^31.  Needs a workspace of rowsel_mfma_workspace_bytes().
 constexpr uint32_t kRowselMfmaMinRows = 16;
 bool rowsel_mfma_eligible(const RowselLaunch& a, uint32_t R);
 size_t rowsel_mfma_workspace_bytes(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1);

@@ -28,10 +28,13 @@
 //    C [k][mi][p]) and a limb split into MFMA A-fragment order, so
 //    each wavefront loads its A fragments as 16-byte vectors.
 //  * The DB stays in the scan layout [p][k][n].  Lane (li, lg) of a B fragment
-//    needs 16 consecutive k of column n0+li; it loads them as 16 dwords (each
-//    load instruction covers 64-byte runs of 4 k-rows) and splits them into the
-//    four limb fragments in registers.  Two column tiles are interleaved so each
-//    128-byte row line is read by back-to-back requests.
+//    needs 16 consecutive k of its column; the two column tiles of a wave take
+//    the even and the odd columns of a 32-column block, so the lane's two
+//    columns are adjacent and each k comes in one 64-bit load (an instruction
+//    covers 128-byte runs of 4 k-rows), addressed by 32-bit offsets from the
+//    point's wave-uniform base.  The words are centred and split into the four
+//    limb fragments in registers (4 ALU ops per word, and a byte transpose of
+//    8 byte-permutes per 4 words).
 //  * Results are written per point, [p][mi][n] (contiguous 64-byte runs), and
 //    a transpose pass produces the p-major output (adding ExpPack's body term
 //    G where the launch carries one).
@@ -46,19 +49,28 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 
 // Centred signed-limb digits of a residue x < q (the byte vector of the
-// centred value's four signed 8-bit digits).
-__device__ __forceinline__ uint32_t centred_digits(uint32_t x, uint32_t q, uint32_t half) {
-  const uint32_t v = x > half ? x - q : x;  // two's complement of x - q when negative
-  return (v + 0x80808080u) ^ 0x80808080u;
+// centred value's four signed 8-bit digits): with v = x - q when x > q/2,
+// digits = (v + 0x80808080) ^ 0x80808080.  The two possible offsets are
+// precomputed (bias_lo = 0x80808080, bias_hi = 0x80808080 - q), so a word
+// costs one compare, one select, one add and one xor.
+__device__ __forceinline__ uint32_t centred_digits(uint32_t x, uint32_t half, uint32_t bias_lo,
+                                                   uint32_t bias_hi) {
+  return (x + (x > half ? bias_hi : bias_lo)) ^ 0x80808080u;
 }
 
-// Four words -> four dwords, dword j holding byte j of words 0..3 (in order).
+// Four words -> four dwords, dword j holding byte j of words a, b, c, d (in
+// that order): a 4x4 byte transpose in two rounds of byte permutes
+// (v_perm_b32 picks bytes 0-3 from its second operand, 4-7 from its first).
 __device__ __forceinline__ void bytes_transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                                  uint32_t o[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = ((a >> (8 * j)) & 0xFFu) | (((b >> (8 * j)) & 0xFFu) << 8) |
-           (((c >> (8 * j)) & 0xFFu) << 16) | (((d >> (8 * j)) & 0xFFu) << 24);
+  const uint32_t ab01 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const uint32_t ab23 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const uint32_t cd01 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  const uint32_t cd23 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  o[0] = __builtin_amdgcn_perm(cd01, ab01, 0x05040100u);           // a0 b0 c0 d0
+  o[1] = __builtin_amdgcn_perm(cd01, ab01, 0x07060302u);           // a1 b1 c1 d1
+  o[2] = __builtin_amdgcn_perm(cd23, ab23, 0x05040100u);           // a2 b2 c2 d2
+  o[3] = __builtin_amdgcn_perm(cd23, ab23, 0x07060302u);           // a3 b3 c3 d3
 }
 
 // 16 digit words (k = 0..15 of one row or column) -> 4 limb fragments.
@@ -96,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void rowsel_limbs_kernel(const uint32_t* 
     for (int t = 0; t < 16; ++t) {
       const uint32_t k = s * 64 + lg * 16 + t;
       const uint32_t x = (mi < m && k < D0) ? ct_t[(p * m + mi) * D0 + k] : 0u;
-      w[t] = centred_digits(x, q, half);  // x = 0 gives digit bytes 0
+      w[t] = centred_digits(x, half, 0x80808080u, 0x80808080u - q);  // x = 0 gives digit bytes 0
     }
     v4i f[4];
     limb_fragments(w, f);
@@ -110,14 +122,42 @@ struct MfmaEpilogue {
   uint32_t corr[kMaxLimbs];  // -(2^31 * sum_d w_d) mod q: undoes the +2^31 offsets
 };
 
+// DB words of one 64-k step into w[nt][t]: 16 consecutive k (from kb) of the
+// lane's column in each tile.  CLAMP: the last step, where rows past D0 are
+// replaced by row D0-1 (the A limbs are zero there, so any valid row serves).
+// PAIR: the lane's two columns are adjacent, so both come in one 64-bit load.
+// Offsets are 32-bit words from the point's (wave-uniform) base.
+template <int NTW, bool PAIR, bool CLAMP>
+__device__ __forceinline__ void load_b_step(const uint32_t* dbp, const uint32_t (&col)[NTW], uint32_t kb,
+                                            uint32_t D0, uint32_t D1, uint32_t (&w)[NTW][16]) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    uint32_t k = kb + t;
+    if constexpr (CLAMP) k = k < D0 ? k : D0 - 1;
+    const uint32_t off = k * D1 + col[0];
+    if constexpr (PAIR) {
+      const uint2 v = *reinterpret_cast<const uint2*>(dbp + off);
+      w[0][t] = v.x;
+      w[1][t] = v.y;
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) w[nt][t] = dbp[off + (col[nt] - col[0])];
+    }
+  }
+}
+
 // One wavefront = one point and NTW column tiles of 16; MT row tiles of 16.
-template <int MT, int NTW>
+// PAIR: tile 0 takes the even and tile 1 the odd columns of a 32-column
+// block (D1 even), so a lane's two columns are one 64-bit word pair.
+template <int MT, int NTW, bool PAIR>
 __global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, MfmaEpilogue ep,
                                                                const v4i* __restrict__ limbs,
                                                                uint32_t* __restrict__ out_t,
                                                                uint32_t m_base, uint32_t nblk,
                                                                uint64_t items, uint32_t S) {
-  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(!PAIR || NTW == 2, "paired columns need two tiles");
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane % 16, lg = lane / 16;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const uint64_t item = (uint64_t)wg * (kThreads / 64) + wave;
@@ -125,17 +165,19 @@ __global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, M
   const uint64_t p = item / nblk;
   const uint32_t n0 = (uint32_t)(item % nblk) * NTW * 16;
   const uint32_t limb = (uint32_t)(p / a.N);
-  const uint32_t q = a.lc.q[limb], half = q / 2;
+  const uint32_t q = a.lc.q[limb], half = q / 2, bias_hi = 0x80808080u - q;
   const uint32_t D0 = a.D0, D1 = a.D1;
 
-  // column of this lane in each tile, clamped (results past D1 are not stored)
-  const uint32_t* dbp = a.dbt + p * (uint64_t)D0 * D1;
-  uint32_t col[NTW];
+  // the column of this lane in tile nt, clamped (results past D1 are not stored)
+  uint32_t col[NTW], cout[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    const uint32_t c = n0 + nt * 16 + li;
-    col[nt] = c < D1 ? c : D1 - 1;
+    const uint32_t c = PAIR ? n0 + 2 * li + nt : n0 + nt * 16 + li;
+    cout[nt] = c;
+    if constexpr (PAIR) col[nt] = (n0 + 2 * li + 1) < D1 ? c : D1 - 2 + nt;  // D1 is even here
+    else col[nt] = c < D1 ? c : D1 - 1;
   }
+  const uint32_t* dbp = a.dbt + p * (uint64_t)D0 * D1;  // D0*D1 < 2^31 words on this path
 
   v4i acc[7][MT][NTW];
 #pragma unroll
@@ -152,20 +194,14 @@ __global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, M
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) af[mt][j] = lp[(((uint64_t)s * MT + mt) * 4 + j) * 64];
-    // 16 consecutive k of each column; past D0 the A limbs are zero, so any
-    // valid row serves
     uint32_t w[NTW][16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      uint32_t k = s * 64 + lg * 16 + t;
-      k = k < D0 ? k : D0 - 1;
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) w[nt][t] = dbp[(uint64_t)k * D1 + col[nt]];
-    }
+    const uint32_t kb = s * 64 + lg * 16;
+    if ((s + 1) * 64 <= D0) load_b_step<NTW, PAIR, false>(dbp, col, kb, D0, D1, w);
+    else load_b_step<NTW, PAIR, true>(dbp, col, kb, D0, D1, w);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) w[nt][t] = centred_digits(w[nt][t], q, half);
+      for (int t = 0; t < 16; ++t) w[nt][t] = centred_digits(w[nt][t], half, 0x80808080u, bias_hi);
       v4i bf[4];
       limb_fragments(w[nt], bf);
 #pragma unroll
@@ -179,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, M
     }
   }
 
-  // Epilogue.  D element e of lane l is (row 4*(l/16) + e, column l%16).
+  // Epilogue.  D element e of lane l is (row 4*(l/16) + e, column l%16 of the tile).
   const uint64_t c32 = a.lc.c[limb], mu = a.lc.mu[limb];
   const uint32_t mrows = a.m - m_base;
 #pragma unroll
@@ -190,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, M
       if (row >= mrows) continue;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        const uint32_t c = n0 + nt * 16 + li;
+        const uint32_t c = cout[nt];
         if (c >= D1) continue;
         uint64_t x = ep.corr[limb];
 #pragma unroll
@@ -230,8 +266,13 @@ hipError_t launch_mfma_pass(const RowselLaunch& a, const MfmaEpilogue& ep, const
   const uint64_t items = a.P * nblk;
   const uint64_t grid = (items + 3) / 4;
   if (grid == 0 || grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((rowsel_mfma_kernel<MT, NTW>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, a,
-                     ep, limbs, out_t, m_base, nblk, items, S);
+  // adjacent column pairs need an even row length (8-byte aligned pairs)
+  if (a.D1 % 2 == 0)
+    hipLaunchKernelGGL((rowsel_mfma_kernel<MT, NTW, true>), dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                       a, ep, limbs, out_t, m_base, nblk, items, S);
+  else
+    hipLaunchKernelGGL((rowsel_mfma_kernel<MT, NTW, false>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                       stream, a, ep, limbs, out_t, m_base, nblk, items, S);
   return hipGetLastError();
 }
 
@@ -245,6 +286,7 @@ uint32_t grid_for(uint64_t items) {
 
 bool rowsel_mfma_eligible(const RowselLaunch& a, uint32_t R) {
   if (a.m < kRowselMfmaMinRows || a.D0 > 16384) return false;
+  if ((uint64_t)a.D0 * a.D1 >= (1ull << 31)) return false;  // 32-bit word offsets within a point
   for (uint32_t r = 0; r < R; ++r)
     if (a.lc.q[r] >= (1u << 31)) return false;
   return true;

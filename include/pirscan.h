@@ -97,7 +97,8 @@ int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor,
  * Workspace bytes pirscan_rowsel_modgemm needs for (shape, m): room for the
  * per-point staging of the output (4 * P * m * D1 bytes, rounded up to 256),
  * and, when the batch runs on int8 MFMA (m >= 16, every modulus < 2^31,
- * D0 <= 16384; GPIR: batching makes RowSel a dense contraction), for the
+ * D0 <= 16384, D0 * D1 < 2^31; GPIR: batching makes RowSel a dense
+ * contraction), for the
  * per-query relayout of ct as well.  0 only on an invalid shape or m == 0.
  */
 size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m);
@@ -155,7 +156,7 @@ int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_p
  * Workspace bytes pirscan_exppack_modgemm needs for (shape, B): room for the
  * per-point staging of the output (4 * P * 2B * Dr bytes, rounded up to 256)
  * and, when the batch runs on int8 MFMA (2B >= 16, every modulus < 2^31,
- * n <= 16384), for the per-query relayout of C.  0 only on an invalid shape
+ * n <= 16384, n * Dr < 2^31), for the per-query relayout of C.  0 only on an invalid shape
  * or B == 0.
  */
 size_t pirscan_exppack_workspace_bytes(const pirscan_exppack_shape* s, uint32_t B);
