@@ -16,9 +16,13 @@ This module is argument marshalling around ``liboracle.so`` (plain C, built by
   term added to each client's second column.
 * :func:`scalar` -- VIPIR's INT8 x INT32 database GEMM mod 2^32 (VIPIR section
   2.5 and section 4), sign-extended DB bytes.
+* :func:`ntt_batch`, :func:`ntt_rns` -- the negacyclic NTT / INTT of every
+  RNS limb of a batch of polynomials by direct evaluation, and the RNS
+  decomposition of integer coefficients followed by the NTT (VIPIR sections
+  2.3, 3.5.2 and 4.3).
 * number-theory helpers (prime search, primitive roots, direct-evaluation
   negacyclic NTT/INTT, schoolbook negacyclic product) and the signed-digit
-  split, used only by the tests that pin the oracle.
+  split, used by the tests that pin the oracle.
 """
 from __future__ import annotations
 
@@ -77,6 +81,12 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [_u32p, _u32p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
             f.restype = None
+        L.oracle_ntt_batch.argtypes = [_u32p, _u32p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                       _u32p, _u32p, ctypes.c_int, ctypes.c_int]
+        L.oracle_ntt_batch.restype = ctypes.c_int
+        L.oracle_ntt_rns.argtypes = [_u32p, _u32p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                     _u32p, _u32p, ctypes.c_int]
+        L.oracle_ntt_rns.restype = ctypes.c_int
         L.oracle_negacyclic_mul.argtypes = [_u32p, _u32p, _u32p, ctypes.c_uint32, ctypes.c_uint32]
         L.oracle_negacyclic_mul.restype = None
         _lib = L
@@ -202,6 +212,38 @@ def intt(A, q: int, psi_: int) -> np.ndarray:
     a = np.empty_like(A)
     lib().oracle_intt(_ptr(A, _u32p), _ptr(a, _u32p), A.size, q, psi_)
     return a
+
+
+def ntt_batch(x, q, psis, inverse: bool = False, nthreads: int = 0) -> np.ndarray:
+    """Forward (or inverse) NTT of every limb of [count][R][N] residue
+    polynomials; limb r uses q[r], psis[r]."""
+    x = _u32(x)
+    R = len(q)
+    if x.ndim != 3 or x.shape[1] != R:
+        raise ValueError("expected [count][R][N]")
+    out = np.empty_like(x)
+    qa, pa = _u32(q), _u32(psis)
+    rc = lib().oracle_ntt_batch(_ptr(x, _u32p), _ptr(out, _u32p), x.shape[0], x.shape[2], R,
+                                _ptr(qa, _u32p), _ptr(pa, _u32p), int(bool(inverse)), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_ntt_batch failed")
+    return out
+
+
+def ntt_rns(coeffs, q, psis, nthreads: int = 0) -> np.ndarray:
+    """RNS decomposition of integer coefficients [count][N] (uint32, read as
+    integers in [0, 2^32)) followed by the NTT: [count][R][N]."""
+    c = _u32(coeffs)
+    if c.ndim != 2:
+        raise ValueError("expected [count][N]")
+    R = len(q)
+    out = np.empty((c.shape[0], R, c.shape[1]), dtype=np.uint32)
+    qa, pa = _u32(q), _u32(psis)
+    rc = lib().oracle_ntt_rns(_ptr(c, _u32p), _ptr(out, _u32p), c.shape[0], c.shape[1], R,
+                              _ptr(qa, _u32p), _ptr(pa, _u32p), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_ntt_rns failed")
+    return out
 
 
 def negacyclic_mul(a, b, q: int) -> np.ndarray:

@@ -328,13 +328,87 @@ void oracle_intt(const uint32_t *A, uint32_t *a, uint32_t N, uint32_t q,
   const uint32_t psi_inv = oracle_powmod(psi, q - 2, q);
   const uint32_t n_inv = oracle_powmod(N % q, q - 2, q);
   for (uint32_t i = 0; i < N; ++i) {
+    /* e_j = psi^-((2j+1) i): e_0 = psi^-i, e_{j+1} = e_j * psi^-2i */
+    const uint32_t step = oracle_powmod(psi_inv, 2ull * i, q);
+    uint32_t e = oracle_powmod(psi_inv, i, q);
     uint64_t acc = 0;
     for (uint32_t j = 0; j < N; ++j) {
-      const uint32_t e = oracle_powmod(psi_inv, (uint64_t)(2ull * j + 1) * i, q);
       acc = (acc + mulmod(A[j] % q, e, q)) % q;
+      e = mulmod(e, step, q);
     }
     a[i] = mulmod((uint32_t)acc, n_inv, q);
   }
+}
+
+/* ---- batched transforms over RNS polynomials ---------------------------- */
+
+typedef struct {
+  const uint32_t *in;
+  uint32_t *out;
+  uint32_t N, R;
+  const uint32_t *q, *psi;
+  int mode; /* 0 forward, 1 inverse, 2 RNS decomposition + forward */
+  uint64_t begin, end; /* limb-polynomial range [begin, end) of count*R */
+} ntt_job;
+
+static void *ntt_worker(void *arg) {
+  const ntt_job *j = (const ntt_job *)arg;
+  uint32_t *tmp = (uint32_t *)malloc(sizeof(uint32_t) * j->N);
+  if (!tmp) return NULL;
+  for (uint64_t lp = j->begin; lp < j->end; ++lp) {
+    const uint64_t c = lp / j->R;
+    const uint32_t r = (uint32_t)(lp % j->R);
+    uint32_t *dst = j->out + lp * j->N; /* out [count][R][N] */
+    if (j->mode == 2) {
+      /* limb r of the coefficient vector: each integer coefficient mod q[r] */
+      const uint32_t *coef = j->in + c * j->N; /* in [count][N] */
+      for (uint32_t i = 0; i < j->N; ++i) tmp[i] = coef[i] % j->q[r];
+      oracle_ntt(tmp, dst, j->N, j->q[r], j->psi[r]);
+    } else if (j->mode == 1) {
+      oracle_intt(j->in + lp * j->N, dst, j->N, j->q[r], j->psi[r]);
+    } else {
+      oracle_ntt(j->in + lp * j->N, dst, j->N, j->q[r], j->psi[r]);
+    }
+  }
+  free(tmp);
+  return NULL;
+}
+
+static int ntt_batch_run(const uint32_t *in, uint32_t *out, uint64_t count, uint32_t N,
+                         uint32_t R, const uint32_t *q, const uint32_t *psi, int mode,
+                         int nthreads) {
+  if (!in || !out || !q || !psi || N == 0 || R == 0) return -1;
+  for (uint32_t r = 0; r < R; ++r)
+    if (q[r] < 2) return -1;
+  const uint64_t items = count * R;
+  if (items == 0) return 0;
+  nthreads = clamp_threads(nthreads, items);
+  pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+  ntt_job *jobs = (ntt_job *)calloc((size_t)nthreads, sizeof(ntt_job));
+  if (!th || !jobs) { free(th); free(jobs); return -1; }
+  for (int t = 0; t < nthreads; ++t) {
+    ntt_job *j = &jobs[t];
+    j->in = in; j->out = out; j->N = N; j->R = R; j->q = q; j->psi = psi; j->mode = mode;
+    j->begin = items * (uint64_t)t / (uint64_t)nthreads;
+    j->end = items * (uint64_t)(t + 1) / (uint64_t)nthreads;
+  }
+  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, ntt_worker, &jobs[t]);
+  ntt_worker(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+  return 0;
+}
+
+int oracle_ntt_batch(const uint32_t *in, uint32_t *out, uint64_t count, uint32_t N,
+                     uint32_t R, const uint32_t *q, const uint32_t *psi, int inverse,
+                     int nthreads) {
+  return ntt_batch_run(in, out, count, N, R, q, psi, inverse ? 1 : 0, nthreads);
+}
+
+int oracle_ntt_rns(const uint32_t *coeffs, uint32_t *out, uint64_t count, uint32_t N,
+                   uint32_t R, const uint32_t *q, const uint32_t *psi, int nthreads) {
+  return ntt_batch_run(coeffs, out, count, N, R, q, psi, 2, nthreads);
 }
 
 void oracle_negacyclic_mul(const uint32_t *a, const uint32_t *b, uint32_t *c,

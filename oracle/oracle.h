@@ -118,9 +118,36 @@ uint32_t oracle_powmod(uint32_t a, uint64_t e, uint32_t q);
  */
 void oracle_ntt(const uint32_t *a, uint32_t *A, uint32_t N, uint32_t q,
                 uint32_t psi);
-/* Inverse: a[i] = N^-1 * sum_j A[j] * psi^-((2j+1) i)  mod q. */
+/* Inverse: a[i] = N^-1 * sum_j A[j] * psi^-((2j+1) i)  mod q, for prime q
+ * (psi^-1 and N^-1 are taken as powers q-2, by Fermat). */
 void oracle_intt(const uint32_t *A, uint32_t *a, uint32_t N, uint32_t q,
                  uint32_t psi);
+
+/*
+ * Batched transforms over RNS polynomials [VIPIR section 2.3: a polynomial of
+ * R_q is an #RNS x N matrix, one row of residues per prime q_r, and the NTT
+ * transforms every row; GPIR: the NTT-domain points of a polynomial are
+ * stored contiguously].  in and out are [count][R][N]: limb r of polynomial
+ * c is the N words at (c*R + r)*N, transformed with q[r] and psi[r] by
+ * oracle_ntt (inverse == 0) or oracle_intt (inverse != 0).  Threads split the
+ * count*R independent limb-polynomials.  Returns 0, or -1 on a null pointer,
+ * zero N or R, or a modulus < 2.
+ */
+int oracle_ntt_batch(const uint32_t *in, uint32_t *out, uint64_t count, uint32_t N,
+                     uint32_t R, const uint32_t *q, const uint32_t *psi, int inverse,
+                     int nthreads);
+
+/*
+ * RNS decomposition followed by the NTT [VIPIR section 3.5.2: each length-N
+ * vector of a first-step output is read as a polynomial whose coefficients
+ * are its integer entries, then transformed; section 4.3 fuses the RNS
+ * decomposition into the NTT]:
+ *   out[c][r][:] = NTT_{q[r], psi[r]}( coeffs[c][i] mod q[r], i < N )
+ * coeffs is [count][N] uint32, each entry the integer in [0, 2^32) it
+ * denotes; out is [count][R][N].  Returns as oracle_ntt_batch.
+ */
+int oracle_ntt_rns(const uint32_t *coeffs, uint32_t *out, uint64_t count, uint32_t N,
+                   uint32_t R, const uint32_t *q, const uint32_t *psi, int nthreads);
 
 /* Schoolbook product in Z_q[X]/(X^N + 1): c = a * b, with X^N = -1. */
 void oracle_negacyclic_mul(const uint32_t *a, const uint32_t *b, uint32_t *c,
