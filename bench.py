@@ -19,6 +19,11 @@ Outside the step, ``next_rows`` measures VIPIR's ExpPack packing GEMM
 H*C + (0|G) (section 3.6 size: N = 2^12, 3 primes, Dr = 256, n = 1280, a
 15 GiB hint) for B = 1 and B = 16 the same way.
 
+Also under ``next_rows``: the negacyclic NTT over the hint's 327680
+polynomials (N = 2^12, three primes) -- the fused RNS decomposition + forward
+transform of 5 GiB of integer coefficients, then the inverse and the forward
+transform in place on the 15 GiB of residues.
+
 The ``cpu_baseline`` leg times the CPU oracle (oracle/, plain C) on a bounded
 sample of each of the four scans and reports the oracle's DB-scan rate for the
 same step mix (and per scan, ExpPack included).
@@ -48,7 +53,12 @@ RS_N, RS_Q = 4096, [536813569, 536690689, 536641537]
 RS_D0 = RS_D1 = 1024
 SC_M = SC_K = 262144
 EP_DR, EP_N = 256, 1280        # ExpPack: output ciphertexts, LWE dimension (same ring as RowSel)
-SEEDS = {"rowsel": 4, "scalar": 5, "exppack": 6}
+# NTT over the hint's polynomials (VIPIR section 3.6: Dr x n polynomials of
+# N = 2^12 over three primes); psi_r = g^((q_r - 1) / 2N) for the smallest
+# generator g of each prime's group
+NTT_PSI = [327210582, 176946644, 321217896]
+NTT_COUNT = EP_DR * EP_N
+SEEDS = {"rowsel": 4, "scalar": 5, "exppack": 6, "ntt": 7}
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "he_database_scan_amd", "csrc")
@@ -61,6 +71,9 @@ KERNEL_SOURCES = {
     "scalar_64GiB_B32": os.path.join(_CSRC, "scalar.hip"),
     "exppack_15GiB_B1": os.path.join(_CSRC, "rowsel.hip"),
     "exppack_15GiB_B16": os.path.join(_CSRC, "rowsel_mfma.hip"),
+    "ntt_rns_fwd_hint": os.path.join(_CSRC, "ntt.hip"),
+    "ntt_inv_hint": os.path.join(_CSRC, "ntt.hip"),
+    "ntt_fwd_hint": os.path.join(_CSRC, "ntt.hip"),
 }
 
 
@@ -132,6 +145,42 @@ class Workloads:
             nws = pirscan.exppack_workspace_bytes(self.eshape, B)
             self.ews[B] = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         torch.cuda.synchronize()
+
+    def setup_ntt(self):
+        """Integer coefficients of the hint's 327680 polynomials (5 GiB) and
+        room for their three-limb transforms (15 GiB)."""
+        torch, pirscan = self.torch, self.pirscan
+        import synth
+
+        dev = torch.device("cuda:0")
+        log("setup: NTT over the hint's polynomials (5 GiB coefficients, 15 GiB residues)")
+        self.nshape = pirscan.NttShape.make(RS_N, RS_Q, NTT_PSI)
+        self.nplan = torch.empty(pirscan.ntt_plan_bytes(self.nshape), dtype=torch.uint8, device=dev)
+        pirscan.ntt_plan_init(self.nshape, self.nplan)
+        self.ncoef = torch.empty((NTT_COUNT, RS_N), dtype=torch.int32, device=dev)
+        synth.fill_uint32_(self.ncoef, SEEDS["ntt"], synth.STREAM_NTT_IN)
+        self.nres = torch.empty((NTT_COUNT, len(RS_Q), RS_N), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    def ntt_scans(self):
+        """The transform on either side of the scans, at the hint's size:
+        fused RNS decomposition + forward NTT (integer coefficients in, three
+        limbs out), then the inverse and the forward NTT in place.  Entries:
+        (callable, residue bytes transformed, algorithmic HBM bytes, polynomials,
+        butterflies, kind)."""
+        pz, sh, plan = self.pirscan, self.nshape, self.nplan
+        R = len(RS_Q)
+        res_b = 4 * NTT_COUNT * R * RS_N
+        coef_b = 4 * NTT_COUNT * RS_N
+        bfly = NTT_COUNT * R * (RS_N // 2) * (RS_N.bit_length() - 1)
+        return {
+            "ntt_rns_fwd_hint": ((lambda: pz.ntt_rns_forward(sh, plan, self.ncoef, self.nres)),
+                                 res_b, coef_b + res_b, NTT_COUNT, bfly, "ntt"),
+            "ntt_inv_hint": ((lambda: pz.ntt_inverse(sh, plan, self.nres, self.nres)),
+                             res_b, 2 * res_b, NTT_COUNT, bfly, "ntt"),
+            "ntt_fwd_hint": ((lambda: pz.ntt_forward(sh, plan, self.nres, self.nres)),
+                             res_b, 2 * res_b, NTT_COUNT, bfly, "ntt"),
+        }
 
     # name -> (callable, DB bytes, algorithmic HBM bytes, queries, macs, kind)
     def scans(self):
@@ -217,6 +266,9 @@ SCAN_KERNELS = {
     "scalar_64GiB_B32": "mfma_kernel<8>",
     "exppack_15GiB_B1": "rowsel_kernel<2,",
     "exppack_15GiB_B16": "rowsel_mfma_kernel<2, 2>",
+    "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
+    "ntt_inv_hint": "ntt_kernel<12, true>",
+    "ntt_fwd_hint": "ntt_kernel<12, false>",
 }
 
 
@@ -345,13 +397,27 @@ def cpu_baseline(budget_s: float = 4.0):
         return (lambda: oracle.exppack(H, C, G, 1, qs, nthreads=threads)), 4 * npts * EP_DR * EP_N, \
             f"{npts} points x {EP_DR}x{EP_N}, B={B}"
 
+    def ntt_sample(kind, npolys):
+        R = len(RS_Q)
+        idx = np.linspace(0, NTT_COUNT - 1, npolys).astype(np.uint64)
+        coef = np.stack([synth.uint32_words(SEEDS["ntt"], synth.STREAM_NTT_IN,
+                                            np.arange(i * RS_N, (i + 1) * RS_N, dtype=np.uint64)) for i in idx])
+        res = oracle.ntt_rns(coef, RS_Q, NTT_PSI, nthreads=threads)
+        fn = {"rns": lambda: oracle.ntt_rns(coef, RS_Q, NTT_PSI, nthreads=threads),
+              "inv": lambda: oracle.ntt_batch(res, RS_Q, NTT_PSI, inverse=True, nthreads=threads),
+              "fwd": lambda: oracle.ntt_batch(res, RS_Q, NTT_PSI, nthreads=threads)}[kind]
+        return fn, 4 * npolys * R * RS_N, f"{npolys} polynomials x {R} limbs x N={RS_N}"
+
     rates, samples = {}, []
     for name, make in (("rowsel_48GiB_B1", lambda: rowsel_sample(2, threads)),
                        ("rowsel_48GiB_B16", lambda: rowsel_sample(32, threads)),
                        ("scalar_64GiB_B1", lambda: scalar_sample(1, 4 * threads)),
                        ("scalar_64GiB_B32", lambda: scalar_sample(32, threads)),
                        ("exppack_15GiB_B1", lambda: exppack_sample(1, threads)),
-                       ("exppack_15GiB_B16", lambda: exppack_sample(16, threads))):
+                       ("exppack_15GiB_B16", lambda: exppack_sample(16, threads)),
+                       ("ntt_rns_fwd_hint", lambda: ntt_sample("rns", threads)),
+                       ("ntt_inv_hint", lambda: ntt_sample("inv", threads)),
+                       ("ntt_fwd_hint", lambda: ntt_sample("fwd", threads))):
         fn, nbytes, what = make()
         reps, t0 = 0, time.perf_counter()
         while True:
@@ -405,6 +471,11 @@ def workload_entry(name, scan, call_ms, kernel_ms):
     srt = sorted(call_ms)
     rf = roofline_for(name, kms, db_bytes, alg_bytes, macs)
     rf["traffic"] = traffic_for(name)
+    if kind == "ntt":
+        return {"ms": ms, "ms_min": srt[0], "ms_median": srt[len(srt) // 2],
+                "kernel": SCAN_KERNELS[name], "kernel_ms": kms, "kernel_ms_min": min(kernel_ms),
+                "polys_per_s": queries / (ms * 1e-3), "residue_GBps": db_bytes / (ms * 1e-3) / 1e9,
+                "butterflies_per_s": macs / (kms * 1e-3), "roofline": rf}
     return {"ms": ms, "ms_min": srt[0], "ms_median": srt[len(srt) // 2],
             "kernel": SCAN_KERNELS[name], "kernel_ms": kms, "kernel_ms_min": min(kernel_ms),
             "db_GBps": db_bytes / (ms * 1e-3) / 1e9, "qps": queries / (ms * 1e-3),
@@ -469,6 +540,12 @@ def main():
     _, ntimes = time_scans(torch, w.pirscan, nscans, args.steps, args.warmup, stream)
     next_rows = {name: workload_entry(name, nscans[name], *ntimes[name]) for name in nscans}
 
+    w.setup_ntt()
+    log("next rows: NTT / INTT over the hint's polynomials")
+    tscans = w.ntt_scans()
+    _, ttimes = time_scans(torch, w.pirscan, tscans, args.steps, args.warmup, stream)
+    ntt_rows = {name: workload_entry(name, tscans[name], *ttimes[name]) for name in tscans}
+
     result = {
         "metric": "effective DB-scan GB/s and QPS at 48/64 GiB DB; % of HBM roofline",
         "value": value,
@@ -492,7 +569,12 @@ def main():
         "workloads": per,
         "next_rows": {"exppack": {"config": {"N": RS_N, "R": len(RS_Q), "Dr": EP_DR, "n": EP_N, "B": [1, 16],
                                              "hint_GiB": 4 * RS_N * len(RS_Q) * EP_DR * EP_N / 2**30},
-                                  "workloads": next_rows}},
+                                  "workloads": next_rows},
+                      "ntt": {"config": {"N": RS_N, "R": len(RS_Q), "q": RS_Q, "psi": NTT_PSI,
+                                         "polynomials": NTT_COUNT,
+                                         "coef_GiB": 4 * NTT_COUNT * RS_N / 2**30,
+                                         "residue_GiB": 4 * NTT_COUNT * len(RS_Q) * RS_N / 2**30},
+                              "workloads": ntt_rows}},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on bounded samples)")

@@ -105,6 +105,31 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
                          uint64_t K, uint32_t B, const ScalarPlan& plan, void* workspace,
                          hipStream_t stream);
 
+// ---- negacyclic NTT over RNS polynomials ------------------------------
+
+struct PsiTable {
+  uint32_t v[kMaxLimbs];  // psi_r: primitive 2N-th root of unity mod q_r
+};
+
+// A validated NTT shape: N = 2^logn in [16, 8192], every q < 2^30 prime with
+// q == 1 (mod 2N), psi^N == -1 (mod q), ninv = N^-1 mod q.
+struct NttDesc {
+  uint32_t N, logn, R;
+  uint32_t q[kMaxLimbs];
+  PsiTable psi;
+  uint32_t ninv[kMaxLimbs];
+};
+
+enum class NttMode { kForward, kInverse, kRnsForward };
+
+// Twiddle tables: [R][2][N] pairs (w, floor(w 2^32 / q)), forward then inverse.
+size_t ntt_plan_bytes(uint32_t N, uint32_t R);
+hipError_t launch_ntt_plan(const NttDesc& d, void* plan, hipStream_t stream);
+// kForward / kInverse: in, out [count][R][N] residues (in == out allowed).
+// kRnsForward: in [count][N] integer coefficients, out [count][R][N].
+hipError_t launch_ntt(const NttDesc& d, NttMode mode, const void* plan, const uint32_t* in, uint32_t* out,
+                      uint64_t count, hipStream_t stream);
+
 // Benchmark hook (pirscan_kernel_timer_begin / _end): when the calling
 // thread has it on, the launchers bracket their main kernel with these two
 // calls, which record a HIP event pair on `stream`.  No-ops otherwise.

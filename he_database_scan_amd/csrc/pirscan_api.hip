@@ -172,6 +172,90 @@ int run_modgemm(const pirscan::RowselLaunch& a, uint32_t R, const Span* bufs, in
   return device_status(pirscan::launch_rowsel(a, workspace, (hipStream_t)stream));
 }
 
+// ---- NTT shape validation (host) -----------------------------------------
+
+uint32_t host_mulmod(uint32_t a, uint32_t b, uint32_t q) { return (uint32_t)(((uint64_t)a * b) % q); }
+
+uint32_t host_powmod(uint32_t b, uint64_t e, uint32_t q) {
+  uint32_t r = 1 % q;
+  b %= q;
+  for (; e; e >>= 1) {
+    if (e & 1) r = host_mulmod(r, b, q);
+    b = host_mulmod(b, b, q);
+  }
+  return r;
+}
+
+// Deterministic primality for 32-bit n: Miller-Rabin to the bases 2, 7 and 61
+// (Jaeschke: no odd composite below 4,759,123,141 is a strong pseudoprime to
+// all three).
+bool host_is_prime(uint32_t n) {
+  if (n < 2) return false;
+  for (uint32_t p : {2u, 3u, 5u, 7u, 11u, 13u, 61u}) {
+    if (n == p) return true;
+    if (n % p == 0) return false;
+  }
+  uint32_t d = n - 1;
+  int s = 0;
+  while ((d & 1) == 0) {
+    d >>= 1;
+    ++s;
+  }
+  for (uint32_t a : {2u, 7u, 61u}) {
+    uint32_t x = host_powmod(a, d, n);
+    if (x == 1 || x == n - 1) continue;
+    bool composite = true;
+    for (int i = 1; i < s && composite; ++i) {
+      x = host_mulmod(x, x, n);
+      if (x == n - 1) composite = false;
+    }
+    if (composite) return false;
+  }
+  return true;
+}
+
+// Validates an NTT shape (N a power of two in [16, 8192]; every q prime,
+// < 2^30, q == 1 mod 2N; psi^N == -1 mod q) and precomputes N^-1 mod q.
+bool ntt_shape_ok(const pirscan_ntt_shape* s, pirscan::NttDesc* d) {
+  if (!s || s->R == 0 || s->R > PIRSCAN_MAX_R) return false;
+  if (s->N < 16 || s->N > 8192 || (s->N & (s->N - 1)) != 0) return false;
+  *d = pirscan::NttDesc{};
+  d->N = s->N;
+  d->R = s->R;
+  while ((1u << d->logn) < s->N) ++d->logn;
+  for (uint32_t r = 0; r < s->R; ++r) {
+    const uint32_t q = s->q[r], psi = s->psi[r];
+    if (q >= (1u << 30) || (q - 1) % (2 * s->N) != 0 || !host_is_prime(q)) return false;
+    if (psi == 0 || psi >= q || host_powmod(psi, s->N, q) != q - 1) return false;
+    d->q[r] = q;
+    d->psi.v[r] = psi;
+    d->ninv[r] = host_powmod(s->N, q - 2, q);  // Fermat: q is prime
+  }
+  return true;
+}
+
+// Runs one transform after the checks every transform shares.
+int run_ntt(const pirscan_ntt_shape* s, pirscan::NttMode mode, const void* plan, const uint32_t* in,
+            uint32_t* out, uint64_t count, void* stream) {
+  pirscan::NttDesc d;
+  if (!ntt_shape_ok(s, &d) || !plan || !in || !out || count == 0) return PIRSCAN_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(plan) % 16) != 0) return PIRSCAN_EINVAL;
+  const unsigned __int128 poly = (unsigned __int128)count * d.N;
+  const unsigned __int128 ow = poly * d.R;
+  const unsigned __int128 iw = mode == pirscan::NttMode::kRnsForward ? poly : ow;
+  if (ow * 4 > kMaxBytes || count > 0x7FFFFFFFull / d.R) return PIRSCAN_EINVAL;
+  const uint64_t plan_b = pirscan::ntt_plan_bytes(d.N, d.R);
+  // in-place is allowed for the residue transforms (every workgroup reads its
+  // whole row before writing it); any other overlap is not
+  const bool same = static_cast<const void*>(in) == static_cast<const void*>(out);
+  if (!(same && mode != pirscan::NttMode::kRnsForward) && overlap(in, (uint64_t)iw * 4, out, (uint64_t)ow * 4))
+    return PIRSCAN_EINVAL;
+  if (overlap(plan, plan_b, out, (uint64_t)ow * 4)) return PIRSCAN_EINVAL;
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  return device_status(pirscan::launch_ntt(d, mode, plan, in, out, count, (hipStream_t)stream));
+}
+
 }  // namespace
 
 namespace pirscan {
@@ -337,6 +421,36 @@ int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* o
   if (dc != PIRSCAN_OK) return dc;
   return device_status(
       pirscan::launch_scalar(db, query, out, M, K, B, p, workspace, (hipStream_t)stream));
+}
+
+size_t pirscan_ntt_plan_bytes(const pirscan_ntt_shape* s) {
+  pirscan::NttDesc d;
+  if (!ntt_shape_ok(s, &d)) return 0;
+  return pirscan::ntt_plan_bytes(d.N, d.R);
+}
+
+int pirscan_ntt_plan_init(const pirscan_ntt_shape* s, void* plan, size_t plan_bytes, void* stream) {
+  pirscan::NttDesc d;
+  if (!ntt_shape_ok(s, &d) || !plan || (reinterpret_cast<uintptr_t>(plan) % 16) != 0) return PIRSCAN_EINVAL;
+  if (plan_bytes < pirscan::ntt_plan_bytes(d.N, d.R)) return PIRSCAN_EINVAL;
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  return device_status(pirscan::launch_ntt_plan(d, plan, (hipStream_t)stream));
+}
+
+int pirscan_ntt_forward(const pirscan_ntt_shape* s, const void* plan, const uint32_t* in, uint32_t* out,
+                        uint64_t count, void* stream) {
+  return run_ntt(s, pirscan::NttMode::kForward, plan, in, out, count, stream);
+}
+
+int pirscan_ntt_inverse(const pirscan_ntt_shape* s, const void* plan, const uint32_t* in, uint32_t* out,
+                        uint64_t count, void* stream) {
+  return run_ntt(s, pirscan::NttMode::kInverse, plan, in, out, count, stream);
+}
+
+int pirscan_ntt_rns_forward(const pirscan_ntt_shape* s, const void* plan, const uint32_t* coeffs,
+                            uint32_t* out, uint64_t count, void* stream) {
+  return run_ntt(s, pirscan::NttMode::kRnsForward, plan, coeffs, out, count, stream);
 }
 
 int pirscan_kernel_timer_begin(uint32_t capacity) {

@@ -65,6 +65,27 @@ class ExppackShape(ctypes.Structure):
         return self.N * self.R
 
 
+class NttShape(ctypes.Structure):
+    """pirscan_ntt_shape: degree N (power of two), R limbs with primes q and
+    primitive 2N-th roots of unity psi."""
+
+    _fields_ = [("N", ctypes.c_uint32), ("R", ctypes.c_uint32), ("q", ctypes.c_uint32 * MAX_R),
+                ("psi", ctypes.c_uint32 * MAX_R)]
+
+    @classmethod
+    def make(cls, N: int, q, psi) -> "NttShape":
+        q = [int(v) for v in q]
+        psi = [int(v) for v in psi]
+        if not 1 <= len(q) <= MAX_R or len(psi) != len(q):
+            raise ValueError(f"need 1..{MAX_R} moduli and one psi per modulus")
+        s = cls()
+        s.N, s.R = N, len(q)
+        for i, (v, w) in enumerate(zip(q, psi)):
+            s.q[i] = v
+            s.psi[i] = w
+        return s
+
+
 class PirscanError(RuntimeError):
     def __init__(self, fn: str, status: int):
         lib = _load()
@@ -107,6 +128,15 @@ def _load():
         L.pirscan_scalar_workspace_bytes.restype = sz
         L.pirscan_scalar_gemm_u32.argtypes = [vp, vp, vp, u64, u64, u32, vp, sz, vp]
         L.pirscan_scalar_gemm_u32.restype = ctypes.c_int
+        nsp = ctypes.POINTER(NttShape)
+        L.pirscan_ntt_plan_bytes.argtypes = [nsp]
+        L.pirscan_ntt_plan_bytes.restype = sz
+        L.pirscan_ntt_plan_init.argtypes = [nsp, vp, sz, vp]
+        L.pirscan_ntt_plan_init.restype = ctypes.c_int
+        for name in ("pirscan_ntt_forward", "pirscan_ntt_inverse", "pirscan_ntt_rns_forward"):
+            f = getattr(L, name)
+            f.argtypes = [nsp, vp, vp, vp, u64, vp]
+            f.restype = ctypes.c_int
         L.pirscan_kernel_timer_begin.argtypes = [u32]
         L.pirscan_kernel_timer_begin.restype = ctypes.c_int
         L.pirscan_kernel_timer_end.argtypes = [ctypes.POINTER(ctypes.c_float), u32, ctypes.POINTER(u32)]
@@ -256,6 +286,48 @@ def scalar_gemm_u32(db, query, out, workspace=None, stream=None) -> None:
            _load().pirscan_scalar_gemm_u32(_ptr(db), _ptr(query), _ptr(out), M, K, B,
                                            _ptr(workspace) if need else ctypes.c_void_p(0),
                                            wbytes, _stream(stream)))
+
+
+def ntt_plan_bytes(shape: NttShape) -> int:
+    return int(_load().pirscan_ntt_plan_bytes(ctypes.byref(shape)))
+
+
+def ntt_plan_init(shape: NttShape, plan, stream=None) -> None:
+    """Fills ``plan`` (a device buffer of at least ``ntt_plan_bytes(shape)``
+    bytes) with the shape's twiddle factors."""
+    if plan.device.type != "cuda":
+        raise ValueError("plan must be a device tensor")
+    nbytes = plan.numel() * plan.element_size()
+    _check("pirscan_ntt_plan_init",
+           _load().pirscan_ntt_plan_init(ctypes.byref(shape), _ptr(plan), nbytes, _stream(stream)))
+
+
+def _ntt_call(name: str, shape: NttShape, plan, x, out, in_words_per_poly: int, stream):
+    N, R = shape.N, shape.R
+    if x.numel() % in_words_per_poly:
+        raise ValueError(f"input of {x.numel()} words is not a whole number of polynomials")
+    count = x.numel() // in_words_per_poly
+    _dev(x, "input", 4, count * in_words_per_poly)
+    _dev(out, "out", 4, count * R * N)
+    _check(name, getattr(_load(), name)(ctypes.byref(shape), _ptr(plan), _ptr(x), _ptr(out), count,
+                                        _stream(stream)))
+
+
+def ntt_forward(shape: NttShape, plan, x, out, stream=None) -> None:
+    """out[c][r][:] = NTT of x[c][r][:] mod q[r] (x, out: [count][R][N] uint32
+    bits; out may be x)."""
+    _ntt_call("pirscan_ntt_forward", shape, plan, x, out, shape.R * shape.N, stream)
+
+
+def ntt_inverse(shape: NttShape, plan, x, out, stream=None) -> None:
+    """Inverse of :func:`ntt_forward` (out may be x)."""
+    _ntt_call("pirscan_ntt_inverse", shape, plan, x, out, shape.R * shape.N, stream)
+
+
+def ntt_rns_forward(shape: NttShape, plan, coeffs, out, stream=None) -> None:
+    """out[c][r][:] = NTT of (coeffs[c][:] mod q[r]): coeffs [count][N] integers
+    in [0, 2^32) as uint32 bits, out [count][R][N]."""
+    _ntt_call("pirscan_ntt_rns_forward", shape, plan, coeffs, out, shape.N, stream)
 
 
 def kernel_timer_begin(capacity: int) -> None:

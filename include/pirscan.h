@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PIRSCAN_VERSION 10100 /* 1.1.0 */
+#define PIRSCAN_VERSION 10200 /* 1.2.0 */
 #define PIRSCAN_MAX_R 8
 
 enum {
@@ -205,6 +205,74 @@ size_t pirscan_scalar_workspace_bytes(uint64_t M, uint64_t K, uint32_t B);
 int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* out,
                             uint64_t M, uint64_t K, uint32_t B,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Negacyclic NTT over RNS polynomials -- the transform on either side of the
+ * scans: it takes first-step outputs and the hint into the point-wise domain
+ * that ExpPack's GEMM consumes (VIPIR section 3.5.2), the plaintext DB into
+ * the NTT-domain points that RowSel scans (GPIR, the OnionPIRv2 background
+ * paragraphs), and results back out.  VIPIR section 2.3: a polynomial of
+ * Z_q[X]/(X^N + 1), q = q_0 ... q_{R-1}, is an R x N matrix of residues, and
+ * the NTT turns polynomial products into point-wise products mod q_r.  For
+ * limb r with psi = psi[r]:
+ *
+ *      forward:  A[j] = sum_{i<N} a[i] * psi^((2j+1) i)          mod q[r]
+ *      inverse:  a[i] = N^-1 * sum_{j<N} A[j] * psi^-((2j+1) i)  mod q[r]
+ *
+ * for j, i < N, both in natural order, canonical results in [0, q[r]).
+ * Layout: [count][R][N] uint32 -- polynomial c's limb r is the N words at
+ * (c*R + r)*N, i.e. each polynomial's P = R*N points contiguous (the p-major
+ * layout RowSel's ct / DB and ExpPack's H, C, G use).  VIPIR section 4.3 runs
+ * an N = 2^12 NTT as one kernel and fuses the RNS decomposition into it;
+ * here every transform is one kernel and pirscan_ntt_rns_forward fuses the
+ * decomposition.
+ */
+typedef struct {
+  uint32_t N;                    /* degree: a power of two in [16, 8192] */
+  uint32_t R;                    /* RNS limbs, 1..PIRSCAN_MAX_R */
+  uint32_t q[PIRSCAN_MAX_R];     /* primes, q[r] < 2^30, q[r] == 1 (mod 2N) */
+  uint32_t psi[PIRSCAN_MAX_R];   /* psi[r]: a primitive 2N-th root of unity mod q[r],
+                                    i.e. psi^N == q[r] - 1 (mod q[r]) */
+} pirscan_ntt_shape;
+
+/* Bytes of the twiddle plan for the shape (16 * R * N), or 0 if the shape is
+ * invalid: N not a power of two in [16, 8192], R out of range, some q[r] not
+ * a prime below 2^30 with q[r] == 1 (mod 2N), or psi[r]^N != -1 (mod q[r]). */
+size_t pirscan_ntt_plan_bytes(const pirscan_ntt_shape* s);
+
+/*
+ * Fills `plan` (device memory, >= pirscan_ntt_plan_bytes(s) bytes, 16-byte
+ * aligned, owned by the caller) with the shape's twiddle factors, on `stream`.
+ * A plan serves every later transform of the same shape (forward, inverse,
+ * RNS) and is read-only to them.  EINVAL on an invalid shape or a short or
+ * misaligned plan.
+ */
+int pirscan_ntt_plan_init(const pirscan_ntt_shape* s, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * Forward / inverse transform of `count` polynomials (count >= 1):
+ *   in  : [count][R][N] uint32 residues, entries < q[r] (precondition, not
+ *         checked; violations give unspecified but memory-safe results).
+ *   out : [count][R][N] uint32, canonical.  out == in (in place) is allowed;
+ *         any other overlap of in, out or plan is EINVAL.
+ *   plan: from pirscan_ntt_plan_init with the same shape.
+ */
+int pirscan_ntt_forward(const pirscan_ntt_shape* s, const void* plan, const uint32_t* in, uint32_t* out,
+                        uint64_t count, void* stream);
+int pirscan_ntt_inverse(const pirscan_ntt_shape* s, const void* plan, const uint32_t* in, uint32_t* out,
+                        uint64_t count, void* stream);
+
+/*
+ * RNS decomposition fused with the forward transform (VIPIR section 3.5.2
+ * reads each length-N vector of integer first-step outputs as a polynomial's
+ * coefficients; section 4.3 fuses the decomposition into the NTT):
+ *   out[c][r][:] = forward transform of ( coeffs[c][i] mod q[r], i < N )
+ *   coeffs : [count][N] uint32, each entry the integer in [0, 2^32) it denotes.
+ *   out    : [count][R][N] uint32, canonical.  Must not overlap coeffs or plan.
+ * The coefficients are read from HBM once for all R limbs.
+ */
+int pirscan_ntt_rns_forward(const pirscan_ntt_shape* s, const void* plan, const uint32_t* coeffs,
+                            uint32_t* out, uint64_t count, void* stream);
 
 /*
  * Benchmark hook for the calling thread (not part of the scan).

@@ -26,6 +26,8 @@ def test_header_declares_the_boundary():
                  "pirscan_scalar_workspace_bytes", "pirscan_layout_db_bytes", "pirscan_strerror",
                  "pirscan_exppack_layout_h", "pirscan_exppack_layout_h_bytes",
                  "pirscan_exppack_workspace_bytes", "pirscan_exppack_modgemm",
+                 "pirscan_ntt_plan_bytes", "pirscan_ntt_plan_init", "pirscan_ntt_forward",
+                 "pirscan_ntt_inverse", "pirscan_ntt_rns_forward",
                  "pirscan_kernel_timer_begin", "pirscan_kernel_timer_end",
                  "pirscan_version", "pirscan_last_device_error"):
         assert want in names
@@ -38,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert pirscan.version() == 10100
+    assert pirscan.version() == 10200
     assert pirscan.strerror(0) == "ok"
     assert "invalid" in pirscan.strerror(-1)
     assert "gfx950" in pirscan.strerror(-3)
@@ -213,3 +215,61 @@ def test_kernel_timer_argument_checks():
     assert L.pirscan_kernel_timer_begin((1 << 20) + 1) == pirscan.EINVAL
     n = ctypes.c_uint32(7)
     assert L.pirscan_kernel_timer_end(None, 0, ctypes.byref(n)) == pirscan.EINVAL   # not begun
+
+
+# primitive 2N-th roots of unity (N = 4096) for the three 29-bit primes: each
+# satisfies psi^N == -1 (mod q), checked here with Python's pow
+PSI3 = [327210582, 176946644, 321217896]
+
+
+def test_ntt_shape_validation_without_a_device():
+    for q, w in zip(Q3, PSI3):
+        assert pow(w, 4096, q) == q - 1
+    s = pirscan.NttShape.make(4096, Q3, PSI3)
+    assert pirscan.ntt_plan_bytes(s) == 16 * 3 * 4096
+    import oracle
+
+    big_q = oracle.ntt_primes(31, 8192, 1)[0]  # a valid NTT prime above 2^30
+    big_psi = oracle.psi(big_q, 4096)
+    assert big_q > (1 << 30) and pow(big_psi, 4096, big_q) == big_q - 1
+    comp = 8193 * 8193                       # == 1 mod 8192, composite, < 2^30
+    assert comp % 8192 == 1 and comp < (1 << 30)
+    bad = [pirscan.NttShape.make(4096, Q3, [PSI3[0], PSI3[1], pow(PSI3[2], 2, Q3[2])]),  # psi^N = 1
+           pirscan.NttShape.make(4096, Q3, [0, PSI3[1], PSI3[2]]),
+           pirscan.NttShape.make(4096, [Q3[0], Q3[1], Q3[2] + 1], PSI3),                  # even modulus
+           pirscan.NttShape.make(4096, [comp], [1]),                                        # composite
+           pirscan.NttShape.make(4096, [1073738753], [536638208]),                          # 1 mod 512 only
+           pirscan.NttShape.make(4096, [big_q], [big_psi]),                                 # >= 2^30
+           pirscan.NttShape.make(3000, Q3, PSI3), pirscan.NttShape.make(8, Q3, PSI3),
+           pirscan.NttShape.make(16384, Q3, PSI3)]
+    for b in bad:
+        assert pirscan.ntt_plan_bytes(b) == 0
+    b = pirscan.NttShape.make(4096, Q3, PSI3)
+    b.R = 0
+    assert pirscan.ntt_plan_bytes(b) == 0
+    b.R = 9
+    assert pirscan.ntt_plan_bytes(b) == 0
+
+
+def test_ntt_rejects_bad_arguments_without_a_device():
+    L = pirscan.lib()
+    s = pirscan.NttShape.make(4096, Q3, PSI3)
+    A, O, PL = 1 << 30, 1 << 40, 1 << 44
+    row = 3 * 4096 * 4                        # bytes of one polynomial (3 limbs)
+    fwd = lambda i, o, c, plan=PL: L.pirscan_ntt_forward(ctypes.byref(s), ctypes.c_void_p(plan),
+                                                         ctypes.c_void_p(i), ctypes.c_void_p(o), c, None)
+    rns = lambda i, o, c, plan=PL: L.pirscan_ntt_rns_forward(ctypes.byref(s), ctypes.c_void_p(plan),
+                                                             ctypes.c_void_p(i), ctypes.c_void_p(o), c, None)
+    assert fwd(A, O, 0) == pirscan.EINVAL                 # zero polynomials
+    assert fwd(0, O, 1) == pirscan.EINVAL
+    assert fwd(A, 0, 1) == pirscan.EINVAL
+    assert fwd(A, O, 1, plan=0) == pirscan.EINVAL
+    assert fwd(A, O, 1, plan=PL + 8) == pirscan.EINVAL    # misaligned plan
+    assert fwd(A, A + 4, 2) == pirscan.EINVAL             # partial overlap
+    assert fwd(A, A + row, 2) == pirscan.EINVAL           # rows shifted by one: still overlapping
+    assert fwd(A, O, 1, plan=O + 64) == pirscan.EINVAL    # plan inside out
+    assert rns(A, A, 1) == pirscan.EINVAL                 # the fused form is never in place
+    assert fwd(A, O, 1 << 62) == pirscan.EINVAL           # size overflow
+    assert L.pirscan_ntt_plan_init(ctypes.byref(s), ctypes.c_void_p(PL), 16 * 3 * 4096 - 1, None) == \
+        pirscan.EINVAL                                     # short plan
+    assert L.pirscan_ntt_plan_init(ctypes.byref(s), ctypes.c_void_p(0), 1 << 20, None) == pirscan.EINVAL
