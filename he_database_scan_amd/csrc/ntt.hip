@@ -48,6 +48,14 @@ __device__ __forceinline__ uint32_t mul_shoup(uint32_t y, uint32_t w, uint32_t w
   return y * w - __umulhi(y, wq) * q;  // in [0, 2q), == y w (mod q)
 }
 
+// -(y w) mod q as a value in (-2q, 0], i.e. the 32-bit word 2^32 - r with
+// r = y w - mulhi(y, w') q in [0, 2q): the same three multiplies as
+// mul_shoup, with the subtraction reversed so that the forward butterfly
+// can form X + r = X - n and X - r + 2q = X + n + 2q in one instruction each.
+__device__ __forceinline__ uint32_t mul_shoup_neg(uint32_t y, uint32_t w, uint32_t wq, uint32_t q) {
+  return __umulhi(y, wq) * q - y * w;
+}
+
 __device__ __forceinline__ uint32_t sub_if_ge(uint32_t x, uint32_t m) {
   const uint32_t d = x - m;
   return d < x ? d : x;  // unsigned min: x - m when x >= m, else x
@@ -59,7 +67,9 @@ __device__ __forceinline__ uint32_t elem_index(uint32_t tid, int e) {
   return (tid & ((1u << LO) - 1)) | ((uint32_t)e << LO) | ((tid >> LO) << (LO + 4));
 }
 
-__device__ __forceinline__ uint32_t bit_reverse(uint32_t x, int n) { return __brev(x) >> (32 - n); }
+// The low n bits of x reversed, n in [0, 32] (n == 0 gives 0; a shift by 32
+// would be undefined).
+__device__ __forceinline__ uint32_t bit_reverse(uint32_t x, int n) { return n ? __brev(x) >> (32 - n) : 0u; }
 
 // One round of forward (CT) stages on index bits BHI down to BLO, with the
 // thread's elements varying in bits [LO, LO+4).  When the thread's index bits
@@ -80,9 +90,9 @@ __device__ __forceinline__ void fwd_round(uint32_t (&x)[kElems], uint32_t tid, c
       else t = m + ((tid >> LO) << (LO + 3 - b)) + (uint32_t)(e >> (b - LO + 1));
       const uint2 w = tw[t];
       const uint32_t X = sub_if_ge(x[e], q2);
-      const uint32_t V = mul_shoup(x[e2], w.x, w.y, q);
-      x[e] = X + V;
-      x[e2] = X - V + q2;
+      const uint32_t nV = mul_shoup_neg(x[e2], w.x, w.y, q);
+      x[e] = X - nV;
+      x[e2] = X + nV + q2;
     }
   }
 }
@@ -110,15 +120,36 @@ __device__ __forceinline__ void inv_round(uint32_t (&x)[kElems], uint32_t tid, c
   }
 }
 
+// LDS word of element e in the mapping with base LO.  When e's bits do not
+// straddle bit 4 (LO == 0 or LO >= 4) the padded index is the padded index
+// of element 0 plus a compile-time step, so each access is one base register
+// and an immediate offset.
+template <int LO>
+__device__ __forceinline__ uint32_t* lds_slot(uint32_t* lds, uint32_t base, uint32_t tid, int e) {
+  if constexpr (LO == 0) return lds + base + e;                                  // pad(16a + e) = 17a + e
+  else if constexpr (LO >= 4) return lds + base + e * ((1 << LO) + (1 << (LO - 4)));
+  else return lds + pad_index((int)elem_index<LO>(tid, e));
+}
+
+template <int LO>
+__device__ __forceinline__ uint32_t lds_base(uint32_t tid) {
+  return (uint32_t)pad_index((int)elem_index<LO>(tid, 0));
+}
+
 // Register <-> LDS exchange between rounds with element mappings LA -> LB.
 template <int LA, int LB>
 __device__ __forceinline__ void exchange(uint32_t (&x)[kElems], uint32_t tid, uint32_t* lds) {
   __syncthreads();  // the previous exchange's reads are done
+  const uint32_t wb = lds_base<LA>(tid), rb = lds_base<LB>(tid);
 #pragma unroll
-  for (int e = 0; e < kElems; ++e) lds[pad_index((int)elem_index<LA>(tid, e))] = x[e];
+  for (int e = 0; e < kElems; ++e) *lds_slot<LA>(lds, wb, tid, e) = x[e];
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kElems; ++e) x[e] = lds[pad_index((int)elem_index<LB>(tid, e))];
+  for (int e = 0; e < kElems; ++e) x[e] = *lds_slot<LB>(lds, rb, tid, e);
+}
+
+__host__ __device__ constexpr int bit_reverse4(int e) {
+  return ((e & 1) << 3) | ((e & 2) << 1) | ((e & 4) >> 1) | ((e & 8) >> 3);
 }
 
 // Round r of the forward transform: bits [hi-4, hi) from the top, hi = LOGN - 4r;
@@ -175,16 +206,26 @@ __device__ __forceinline__ void forward_and_store(uint32_t (&x)[kElems], uint32_
   // canonical, then to natural order: element j holds A[bitrev(j)]
   constexpr int LL = last_fwd_lo<LOGN>();
   __syncthreads();
+  if constexpr (LL == 0 && LOGN >= 8) {
+    // element j = 16 tid + e goes to bitrev(j) = bitrev4(e) 2^(n-4) + bitrev_{n-4}(tid)
+    const uint32_t wb = (uint32_t)pad_index((int)bit_reverse(tid, LOGN - 4));
 #pragma unroll
-  for (int e = 0; e < kElems; ++e) {
-    const uint32_t v = sub_if_ge(sub_if_ge(x[e], 2 * q), q);
-    lds[pad_index((int)bit_reverse(elem_index<LL>(tid, e), LOGN))] = v;
+    for (int e = 0; e < kElems; ++e)
+      lds[wb + bit_reverse4(e) * ((1 << (LOGN - 4)) + (1 << (LOGN - 8)))] = sub_if_ge(sub_if_ge(x[e], 2 * q), q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kElems; ++e) {
+      const uint32_t v = sub_if_ge(sub_if_ge(x[e], 2 * q), q);
+      lds[pad_index((int)bit_reverse(elem_index<LL>(tid, e), LOGN))] = v;
+    }
   }
   __syncthreads();
+  const uint32_t rb = (uint32_t)pad_index((int)tid);
 #pragma unroll
   for (int e = 0; e < kElems; ++e) {
     const uint32_t j = tid + T * (uint32_t)e;
-    dst[j] = lds[pad_index((int)j)];
+    if constexpr (T >= 16) dst[j] = lds[rb + e * (T + T / 16)];
+    else dst[j] = lds[pad_index((int)j)];
   }
 }
 
@@ -221,11 +262,15 @@ __global__ __launch_bounds__(1 << (LOGN - 4)) void ntt_kernel(NttArgs a) {
     // scatter the natural-order input to bit-reversed positions
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = __builtin_nontemporal_load(src + tid + T * (uint32_t)e);
+    // bitrev(tid + T e) = 16 bitrev_{n-4}(tid) + bitrev4(e): padded, 17 bitrev_{n-4}(tid) + bitrev4(e)
+    const uint32_t sb = 17 * bit_reverse(tid, LOGN - 4);
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) lds[pad_index((int)bit_reverse(tid + T * (uint32_t)e, LOGN))] = x[e];
+    for (int e = 0; e < kElems; ++e) lds[sb + bit_reverse4(e)] = x[e];
     __syncthreads();
+    constexpr int L0 = InvRound<LOGN, 0>::lo;
+    const uint32_t rb = lds_base<L0>(tid);
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) x[e] = lds[pad_index((int)elem_index<InvRound<LOGN, 0>::lo>(tid, e))];
+    for (int e = 0; e < kElems; ++e) x[e] = *lds_slot<L0>(lds, rb, tid, e);
     inv_rounds_from<LOGN, 0>(x, tid, tw, q, lds);
     // the last round's mapping is lo = LOGN - 4: element e sits at tid + T e
     static_assert(InvRound<LOGN, (LOGN + 3) / 4 - 1>::lo == LOGN - 4, "inverse ends coalesced");
