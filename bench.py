@@ -58,6 +58,20 @@ EP_DR, EP_N = 256, 1280        # ExpPack: output ciphertexts, LWE dimension (sam
 # generator g of each prime's group
 NTT_PSI = [327210582, 176946644, 321217896]
 NTT_COUNT = EP_DR * EP_N
+# the scalar product at the pages' other shapes, on the 64 GiB database's bytes:
+# VIPIR's hint DB * A (D/D0 = 2^20, n = 1280), the double-packing second fold
+# (8N x D1 INT8 times D1 x (n+1), D1 = 2^17), and D/D0 = 2^20, 2^19, 2^17
+N_LWE = 1280
+SHAPE_SCANS = {
+    "scalar_hint_64GiB_n1280": (1 << 20, 1 << 16, N_LWE),
+    "scalar_fold2_4GiB_n1281": (8 * RS_N, 1 << 17, N_LWE + 1),
+    "scalar_64GiB_D1_2e20_B1": (1 << 20, 1 << 16, 1),
+    "scalar_64GiB_D1_2e20_B32": (1 << 20, 1 << 16, 32),
+    "scalar_64GiB_D1_2e19_B1": (1 << 19, 1 << 17, 1),
+    "scalar_64GiB_D1_2e19_B32": (1 << 19, 1 << 17, 32),
+    "scalar_64GiB_D1_2e17_B1": (1 << 17, 1 << 19, 1),
+    "scalar_64GiB_D1_2e17_B32": (1 << 17, 1 << 19, 32),
+}
 SEEDS = {"rowsel": 4, "scalar": 5, "exppack": 6, "ntt": 7}
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -71,6 +85,7 @@ KERNEL_SOURCES = {
     "scalar_64GiB_B32": os.path.join(_CSRC, "scalar.hip"),
     "exppack_15GiB_B1": os.path.join(_CSRC, "rowsel.hip"),
     "exppack_15GiB_B16": os.path.join(_CSRC, "rowsel_mfma.hip"),
+    **{name: os.path.join(_CSRC, "scalar.hip") for name in SHAPE_SCANS},
     "ntt_rns_fwd_hint": os.path.join(_CSRC, "ntt.hip"),
     "ntt_inv_hint": os.path.join(_CSRC, "ntt.hip"),
     "ntt_fwd_hint": os.path.join(_CSRC, "ntt.hip"),
@@ -182,6 +197,25 @@ class Workloads:
                              res_b, 2 * res_b, NTT_COUNT, bfly, "ntt"),
         }
 
+    def shape_scans(self):
+        """The scalar product at the hint, second-fold and aspect-ratio shapes,
+        each on the leading M*K bytes of the 64 GiB database buffer."""
+        torch, pz = self.torch, self.pirscan
+        import synth
+
+        dev = torch.device("cuda:0")
+        flat = self.sdb.view(-1)
+        out = {}
+        for name, (M, K, B) in SHAPE_SCANS.items():
+            db = flat[:M * K].view(M, K)
+            q = torch.empty((K, B), dtype=torch.int32, device=dev)
+            synth.fill_uint32_(q, SEEDS["scalar"], synth.STREAM_SCALAR_Q)
+            o = torch.empty((M, B), dtype=torch.int32, device=dev)
+            ws = torch.empty(pz.scalar_workspace_bytes(M, K, B), dtype=torch.uint8, device=dev)
+            out[name] = ((lambda db=db, q=q, o=o, ws=ws: pz.scalar_gemm_u32(db, q, o, ws)),
+                         M * K, M * K + 4 * K * B + 4 * M * B, B, M * K * B, "scalar")
+        return out
+
     # name -> (callable, DB bytes, algorithmic HBM bytes, queries, macs, kind)
     def scans(self):
         P = RS_N * len(RS_Q)
@@ -220,7 +254,10 @@ class Workloads:
 # int8 MACs the MFMA paths issue per algorithmic MAC: the scalar B>1 GEMM
 # multiplies 4 query digit planes; batched RowSel / ExpPack multiply 4 x 4
 # limb pairs.
-MFMA_MACS_PER_MAC = {"rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4, "exppack_15GiB_B16": 16}
+MFMA_MACS_PER_MAC = {"rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4, "exppack_15GiB_B16": 16,
+                     **{name: 4 for name, (M, K, B) in SHAPE_SCANS.items() if B > 1}}
+# shapes whose int8 MFMA work exceeds what HBM time allows: priced against the MFMA peak
+MFMA_BOUND = {"scalar_hint_64GiB_n1280", "scalar_fold2_4GiB_n1281"}
 
 
 def roofline_for(name, ms, db_bytes, alg_bytes, macs):
@@ -232,6 +269,10 @@ def roofline_for(name, ms, db_bytes, alg_bytes, macs):
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     rf = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
           "frac": achieved / HBM_PEAK_GBS}
+    if name in MFMA_BOUND:
+        tops = 2 * macs * MFMA_MACS_PER_MAC[name] / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": tops, "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": tops / MFMA_INT8_PEAK_TOPS, "hbm_GBps": achieved}
     if name in MFMA_MACS_PER_MAC:
         tops = 2 * macs * MFMA_MACS_PER_MAC[name] / (ms * 1e-3) / 1e12
         rf["mfma_int8_TOPS"] = tops
@@ -266,6 +307,7 @@ SCAN_KERNELS = {
     "scalar_64GiB_B32": "mfma_kernel<8>",
     "exppack_15GiB_B1": "rowsel_kernel<2,",
     "exppack_15GiB_B16": "rowsel_mfma_kernel<2, 2>",
+    **{name: ("gemv_kernel" if B == 1 else "mfma_kernel<8>") for name, (M, K, B) in SHAPE_SCANS.items()},
     "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
     "ntt_inv_hint": "ntt_kernel<12, true>",
     "ntt_fwd_hint": "ntt_kernel<12, false>",
@@ -540,6 +582,14 @@ def main():
     _, ntimes = time_scans(torch, w.pirscan, nscans, args.steps, args.warmup, stream)
     next_rows = {name: workload_entry(name, nscans[name], *ntimes[name]) for name in nscans}
 
+    log("next rows: scalar product at the hint, second-fold and D/D0 shapes")
+    sscans = w.shape_scans()
+    nsteps = min(args.steps, 3)
+    _, stimes = time_scans(torch, w.pirscan, sscans, nsteps, 1, stream)
+    shape_rows = {name: workload_entry(name, sscans[name], *stimes[name]) for name in sscans}
+    del sscans
+    torch.cuda.empty_cache()
+
     w.setup_ntt()
     log("next rows: NTT / INTT over the hint's polynomials")
     tscans = w.ntt_scans()
@@ -570,6 +620,9 @@ def main():
         "next_rows": {"exppack": {"config": {"N": RS_N, "R": len(RS_Q), "Dr": EP_DR, "n": EP_N, "B": [1, 16],
                                              "hint_GiB": 4 * RS_N * len(RS_Q) * EP_DR * EP_N / 2**30},
                                   "workloads": next_rows},
+                      "scalar_shapes": {"config": {name: {"M": M, "K": K, "B": B}
+                                                   for name, (M, K, B) in SHAPE_SCANS.items()},
+                                        "steps": nsteps, "workloads": shape_rows},
                       "ntt": {"config": {"N": RS_N, "R": len(RS_Q), "q": RS_Q, "psi": NTT_PSI,
                                          "polynomials": NTT_COUNT,
                                          "coef_GiB": 4 * NTT_COUNT * RS_N / 2**30,

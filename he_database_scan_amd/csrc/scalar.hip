@@ -221,11 +221,20 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const uint32_t* __
 //    slot consumed by a step is refilled with the step kMfmaDepth ahead, so
 //    ~kMfmaDepth * 2 KiB per wavefront are in flight without extra registers.
 // ---------------------------------------------------------------------------
+#ifndef PIRSCAN_SCALAR_MFMA_DEPTH
+#define PIRSCAN_SCALAR_MFMA_DEPTH 8
+#endif
+#ifndef PIRSCAN_SCALAR_MFMA_CHUNK
+#define PIRSCAN_SCALAR_MFMA_CHUNK 4
+#endif
+#ifndef PIRSCAN_SCALAR_MFMA_ROWTILES
+#define PIRSCAN_SCALAR_MFMA_ROWTILES 2
+#endif
 constexpr int kMfmaWaves = 8;
-constexpr int kMfmaRowTiles2 = 2;                  // 2 x 16 rows per wavefront
-constexpr int kMfmaDepth = 8;                      // A ring depth in 64-k steps
-static_assert(kMfmaDepth % 4 == 0, "the ring turns in whole B chunks");
-constexpr int kMfmaChunkSteps = 4;                 // B chunk = 4 steps = 256 k
+constexpr int kMfmaRowTiles2 = PIRSCAN_SCALAR_MFMA_ROWTILES;  // 16-row tiles per wavefront
+constexpr int kMfmaDepth = PIRSCAN_SCALAR_MFMA_DEPTH;        // A ring depth in 64-k steps
+constexpr int kMfmaChunkSteps = PIRSCAN_SCALAR_MFMA_CHUNK;   // B chunk = 4 steps = 256 k
+static_assert(kMfmaDepth % kMfmaChunkSteps == 0, "the ring turns in whole B chunks");
 constexpr uint64_t kMfmaChunkK = 64 * kMfmaChunkSteps;
 
 template <int NT>
