@@ -530,6 +530,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-shapes", action="store_true",
+                    help="leave out the scalar hint / second-fold / D/D0 rows (profiling runs: their MFMA "
+                         "launches share one grid size with the step's B=32 scan)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one torch copy of this many GiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -582,13 +585,15 @@ def main():
     _, ntimes = time_scans(torch, w.pirscan, nscans, args.steps, args.warmup, stream)
     next_rows = {name: workload_entry(name, nscans[name], *ntimes[name]) for name in nscans}
 
-    log("next rows: scalar product at the hint, second-fold and D/D0 shapes")
-    sscans = w.shape_scans()
     nsteps = min(args.steps, 3)
-    _, stimes = time_scans(torch, w.pirscan, sscans, nsteps, 1, stream)
-    shape_rows = {name: workload_entry(name, sscans[name], *stimes[name]) for name in sscans}
-    del sscans
-    torch.cuda.empty_cache()
+    shape_rows = None
+    if not args.skip_shapes:
+        log("next rows: scalar product at the hint, second-fold and D/D0 shapes")
+        sscans = w.shape_scans()
+        _, stimes = time_scans(torch, w.pirscan, sscans, nsteps, 1, stream)
+        shape_rows = {name: workload_entry(name, sscans[name], *stimes[name]) for name in sscans}
+        del sscans
+        torch.cuda.empty_cache()
 
     w.setup_ntt()
     log("next rows: NTT / INTT over the hint's polynomials")

@@ -117,6 +117,64 @@ __global__ __launch_bounds__(kThreads) void rowsel_limbs_kernel(const uint32_t* 
   }
 }
 
+// ct(mi, k, p) -> A fragments [p][s][mt][limb][lane] in one pass, for rows
+// m_base .. m_base + 16*MT: one workgroup per (32 points, step s, row tile
+// mt, k-group lg).  The 16 rows x 16 k of the tile are read as 256 runs of
+// 32 points (128 contiguous bytes each) into LDS, then each thread forms the
+// fragment lanes (li, lg) of points p: 16 words (k = 64 s + 16 lg + t) ->
+// centred signed limbs -> 4 x 16 bytes, written as 256-byte runs per point
+// and limb.  Rows past m and k past D0 are zero.  Needs P % 4 == 0 and a
+// 16-byte aligned ct with strides that are multiples of 4 words.
+// LDS word of (row r, point p): r*32 + ((p + 4*(r/16)) mod 32), which keeps
+// both the 16-byte row stores and the per-thread column reads at two-way
+// bank conflicts at most.
+constexpr int kPrepPoints = 32;
+__global__ __launch_bounds__(kThreads) void rowsel_prep_kernel(RowselLaunch a, v4i* __restrict__ limbs,
+                                                               uint32_t m_base, uint32_t MT, uint32_t S,
+                                                               uint32_t pblocks) {
+  __shared__ uint32_t tile[256 * kPrepPoints];
+  const uint32_t tid = threadIdx.x;
+  uint32_t id = blockIdx.x;
+  const uint32_t pb = id % pblocks;
+  id /= pblocks;
+  const uint32_t lg = id % 4;
+  id /= 4;
+  const uint32_t mt = id % MT;
+  const uint32_t s = id / MT;
+  const uint64_t p0 = (uint64_t)pb * kPrepPoints;
+  // load: row r = li*16 + t (mi = m_base + 16 mt + li, k = 64 s + 16 lg + t), 8 threads x 16 B per row
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const uint32_t r = pass * 32 + tid / 8, c4 = (tid % 8) * 4;
+    const uint32_t mi = m_base + mt * 16 + r / 16, k = s * 64 + lg * 16 + r % 16;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (mi < a.m && k < a.D0 && p0 + c4 < a.P)
+      v = *reinterpret_cast<const uint4*>(a.ct + mi * a.ct_sm + (uint64_t)k * a.ct_sk + p0 + c4);
+    *reinterpret_cast<uint4*>(&tile[r * kPrepPoints + ((c4 + 4 * (r / 16)) % kPrepPoints)]) = v;
+  }
+  __syncthreads();
+  // form: thread -> (li = tid % 16, point pair), two points per thread
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t li = tid % 16, pp = h * 16 + tid / 16;
+    const uint64_t p = p0 + pp;
+    if (p >= a.P) continue;
+    const uint32_t q = a.lc.q[p / a.N], half = q / 2;
+    uint32_t w[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t r = li * 16 + t;
+      w[t] = centred_digits(tile[r * kPrepPoints + ((pp + 4 * li) % kPrepPoints)], half, 0x80808080u,
+                            0x80808080u - q);
+    }
+    v4i f[4];
+    limb_fragments(w, f);
+    v4i* dst = limbs + (((p * S + s) * MT + mt) * 4) * 64 + li + 16 * lg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j * 64] = f[j];
+  }
+}
+
 struct MfmaEpilogue {
   uint32_t w[kMaxLimbs][7];  // 2^(8d) mod q
   uint32_t corr[kMaxLimbs];  // -(2^31 * sum_d w_d) mod q: undoes the +2^31 offsets
@@ -316,7 +374,29 @@ hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace
     ep.corr[r] = (uint32_t)((q - off) % q);
   }
 
-  // ct(mi, k, p) -> ct_t [P][m][D0]
+  // ct -> A fragments in one pass where the 16-byte point runs are aligned
+  const bool fused = a.P % 4 == 0 && a.ct_sm % 4 == 0 && a.ct_sk % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(a.ct) % 16 == 0;
+  hipError_t e = hipSuccess;
+  if (fused) {
+    const uint64_t pblocks = (a.P + kPrepPoints - 1) / kPrepPoints;
+    for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
+      const uint32_t MT = a.m - m_base > 16 ? 2 : 1;
+      const uint64_t grid = pblocks * 4 * MT * S;
+      if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(rowsel_prep_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a, limbs,
+                         m_base, MT, S, (uint32_t)pblocks);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      timer_mark_start(stream);  // first pass only
+      if (MT == 2) e = launch_mfma_pass<2, 2>(a, ep, limbs, out_t, m_base, S, stream);
+      else e = launch_mfma_pass<1, 2>(a, ep, limbs, out_t, m_base, S, stream);
+      if (e != hipSuccess) return e;
+    }
+    timer_mark_stop(stream);
+    return launch_out_relayout(a, out_t, stream);
+  }
+
+  // otherwise: ct(mi, k, p) -> ct_t [P][m][D0], then the limb split
   TransposeDesc tc{};
   tc.src = a.ct;
   tc.dst = ct_t;
@@ -327,7 +407,7 @@ hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace
   tc.s_row = a.ct_sk;
   tc.d_batch = a.D0;
   tc.d_row = (uint64_t)a.m * a.D0;
-  hipError_t e = launch_transpose(tc, stream);
+  e = launch_transpose(tc, stream);
   if (e != hipSuccess) return e;
   for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
     const uint32_t rows = a.m - m_base;

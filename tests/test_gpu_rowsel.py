@@ -188,3 +188,17 @@ def test_batched_path_edges(q, m, D0, D1):
         ctv = np.broadcast_to(vals.astype(np.uint32), (m, D0, P)).copy()
         dbv = np.broadcast_to(((qv - 1) - vals % qv).astype(np.uint32), (D0, D1, P)).copy()
         np.testing.assert_array_equal(run_gpu(ctv, dbv, N, q), oracle.rowsel(ctv, dbv, N, q))
+
+
+@pytest.mark.parametrize("N,q,m,D0,D1", [(3, [2147483647, 65537], 32, 70, 48), (5, MED_Q, 20, 130, 66),
+                                         (16, [1073741827, 7681], 48, 200, 40)])
+def test_batched_path_point_counts(N, q, m, D0, D1):
+    """P = R*N not a multiple of 4 (the ct relayout then goes through the
+    transpose + limb-split passes) and P not a multiple of the 32-point prep
+    block, with one, two and three row-tile passes."""
+    P = N * len(q)
+    rng = np.random.default_rng(N * 1000 + m)
+    say(f"rowsel batched N={N} P={P} m={m} D0={D0} D1={D1}")
+    ct = rand_res(rng, (m, D0, P), N, q)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))
