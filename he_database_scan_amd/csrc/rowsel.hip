@@ -83,6 +83,59 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeDesc t, ui
   }
 }
 
+// The same transpose with 16-byte accesses on both sides, for the common case
+// where every extent, stride and base pointer is a multiple of 4 words: a
+// thread reads 4 consecutive columns of a source row and writes 4
+// consecutive rows of a destination row, so a wavefront moves 1 KiB per
+// global instruction instead of 256 bytes.  The tile stays 64 x 64 words
+// (padded rows keep the LDS column reads at two-way bank conflicts).
+typedef uint32_t u32x4t __attribute__((ext_vector_type(4)));
+
+template <bool kAdd>
+__global__ __launch_bounds__(kThreads) void transpose4_kernel(TransposeDesc t, uint64_t tiles_c,
+                                                              uint64_t tiles_rc, uint64_t tiles) {
+  __shared__ uint32_t tile[kTile][kTile + 1];
+  const int c4 = (threadIdx.x % 16) * 4, ty = threadIdx.x / 16;  // 16 threads per 64-word row
+  for (uint64_t id = blockIdx.x; id < tiles; id += gridDim.x) {
+    const uint64_t b = id / tiles_rc, rc = id % tiles_rc;
+    const uint64_t c0 = (rc % tiles_c) * kTile, r0 = (rc / tiles_c) * kTile;
+    const uint32_t* src = t.src + b * t.s_batch;
+#pragma unroll
+    for (int i = ty; i < kTile; i += kThreads / 16) {
+      const uint64_t r = r0 + i, c = c0 + c4;
+      u32x4t v = {0u, 0u, 0u, 0u};
+      if (r < t.rows && c < t.cols) v = *reinterpret_cast<const u32x4t*>(src + r * t.s_row + c);
+      tile[i][c4] = v.x;
+      tile[i][c4 + 1] = v.y;
+      tile[i][c4 + 2] = v.z;
+      tile[i][c4 + 3] = v.w;
+    }
+    __syncthreads();
+    uint32_t* dst = t.dst + b * t.d_batch;
+#pragma unroll
+    for (int i = ty; i < kTile; i += kThreads / 16) {
+      const uint64_t c = c0 + i, r = r0 + c4;
+      if (c < t.cols && r < t.rows) {
+        u32x4t v = {tile[c4][i], tile[c4 + 1][i], tile[c4 + 2][i], tile[c4 + 3][i]};
+        if constexpr (kAdd) {
+          if (b & 1) {  // (0 | G): the body term goes to each client's second column
+            const u32x4t g = *reinterpret_cast<const u32x4t*>(t.add + (b >> 1) * t.add_b + c * t.add_c + r);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint64_t q = t.lc.q[(r + j) / t.N];
+              uint64_t x = (uint64_t)v[j] + g[j];
+              if (x >= q) x -= q;
+              v[j] = (uint32_t)x;
+            }
+          }
+        }
+        *reinterpret_cast<u32x4t*>(dst + c * t.d_row + r) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // R2-R4: the scan.
 // ---------------------------------------------------------------------------
@@ -354,12 +407,24 @@ hipError_t launch_transpose(const TransposeDesc& t, hipStream_t stream) {
   const uint64_t tiles_c = (t.cols + kTile - 1) / kTile, tiles_r = (t.rows + kTile - 1) / kTile;
   const uint64_t tiles_rc = tiles_c * tiles_r, tiles = tiles_rc * t.batch;
   const uint64_t grid = tiles < (1ull << 20) ? tiles : (1ull << 20);
-  if (t.add)
+  auto a16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+  const bool vec4 = t.rows % 4 == 0 && t.cols % 4 == 0 && t.s_row % 4 == 0 && t.s_batch % 4 == 0 &&
+                    t.d_row % 4 == 0 && t.d_batch % 4 == 0 && a16(t.src) && a16(t.dst) &&
+                    (!t.add || (t.add_b % 4 == 0 && t.add_c % 4 == 0 && a16(t.add)));
+  if (vec4) {
+    if (t.add)
+      hipLaunchKernelGGL(transpose4_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, t,
+                         tiles_c, tiles_rc, tiles);
+    else
+      hipLaunchKernelGGL(transpose4_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, t,
+                         tiles_c, tiles_rc, tiles);
+  } else if (t.add) {
     hipLaunchKernelGGL(transpose_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, t,
                        tiles_c, tiles_rc, tiles);
-  else
+  } else {
     hipLaunchKernelGGL(transpose_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, t,
                        tiles_c, tiles_rc, tiles);
+  }
   return hipGetLastError();
 }
 
