@@ -302,11 +302,11 @@ def traffic_for(name):
 # first in dispatch order.
 SCAN_KERNELS = {
     "rowsel_48GiB_B1": "rowsel_kernel<2,",
-    "rowsel_48GiB_B16": "rowsel_mfma_kernel<2, 2>",
+    "rowsel_48GiB_B16": "rowsel_mfma_kernel<2, 2",
     "scalar_64GiB_B1": "gemv_kernel",
     "scalar_64GiB_B32": "mfma_kernel<8>",
     "exppack_15GiB_B1": "rowsel_kernel<2,",
-    "exppack_15GiB_B16": "rowsel_mfma_kernel<2, 2>",
+    "exppack_15GiB_B16": "rowsel_mfma_kernel<2, 2",
     **{name: ("gemv_kernel" if B == 1 else "mfma_kernel<8>") for name, (M, K, B) in SHAPE_SCANS.items()},
     "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
     "ntt_inv_hint": "ntt_kernel<12, true>",
