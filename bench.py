@@ -43,6 +43,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+# 32-bit integer VALU rate of the multiply / min / select class: 256 CUs x 4
+# SIMDs x 16 lanes per clock x 2.4 GHz (a probe measured v_mul_lo_u32,
+# v_mul_hi_u32 and v_min_u32 at this rate and v_add_u32 at twice it)
+VALU_INT32_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# integer operations per lazy (Harvey) butterfly with a Shoup product: three
+# 32-bit multiplies and a subtraction for the twiddle product, a compare-and-
+# subtract pair to keep one input below 2q, and one operation per output
+NTT_OPS_PER_BUTTERFLY = 8
 MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (ops = 2 x MAC)
 # VALU 32x32->64-bit multiply-add (v_mad_u64_u32): 256 CUs x 4 SIMDs x 16
 # lanes per clock x 2.4 GHz = 39.3e12 MAC/s (half the issue rate of simple
@@ -269,6 +277,11 @@ def roofline_for(name, ms, db_bytes, alg_bytes, macs):
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     rf = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
           "frac": achieved / HBM_PEAK_GBS}
+    if name.startswith("ntt_"):
+        # macs = butterflies per launch; the NTT kernels are bound by integer ALU issue
+        tops = NTT_OPS_PER_BUTTERFLY * macs / (ms * 1e-3) / 1e12
+        return {"bound": "alu", "achieved": tops, "peak": VALU_INT32_PEAK_TOPS, "unit": "TOP/s",
+                "frac": tops / VALU_INT32_PEAK_TOPS, "hbm_GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS}
     if name in MFMA_BOUND:
         tops = 2 * macs * MFMA_MACS_PER_MAC[name] / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": tops, "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOP/s",
