@@ -36,6 +36,7 @@ constexpr uint64_t kGemvKBlock = 64 * 16 * kGemvJ;  // 4096
 constexpr int kGemvRowsPerWave = 64;
 constexpr int kGemvRowBatch = 4;
 constexpr uint64_t kMfmaKBlockMax = 16384;
+constexpr uint32_t kMfmaMaxCols = 64;  // query columns per MFMA pass (4 digit planes each)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -239,6 +240,10 @@ constexpr uint64_t kMfmaChunkK = 64 * kMfmaChunkSteps;
 
 template <int NT>
 struct MfmaShape {
+  // A ring depth: 8 steps, or 4 for the widest passes, whose 16 column tiles
+  // of accumulators leave fewer registers for the ring
+  static constexpr int DEPTH = NT >= 16 ? 4 : kMfmaDepth;
+  static_assert(DEPTH % kMfmaChunkSteps == 0, "the ring turns in whole B chunks");
   static constexpr int HT = NT / 4;                        // column tiles per digit plane
   static constexpr int DCOLS = 16 * NT;                    // 4 * bpad digit columns
   static constexpr int CHUNK_BYTES = kMfmaChunkK * DCOLS;  // 32 KiB at bpad = 32
@@ -258,6 +263,7 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
   constexpr int DCOLS = MfmaShape<NT>::DCOLS;
   constexpr int CHUNK_BYTES = MfmaShape<NT>::CHUNK_BYTES;
   constexpr int PIECES = MfmaShape<NT>::PIECES;
+  constexpr int DEPTH = MfmaShape<NT>::DEPTH;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t row0 = (rb * kMfmaWaves + wave) * (16 * kMfmaRowTiles2);
@@ -290,9 +296,9 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
     for (int ct = 0; ct < NT; ++ct) acc[rt][ct] = v4i{0, 0, 0, 0};
 
   // prologue: A ring for steps 0..depth-1, B chunk 0 into LDS
-  v4i a[kMfmaDepth][kMfmaRowTiles2];
+  v4i a[DEPTH][kMfmaRowTiles2];
 #pragma unroll
-  for (int d = 0; d < kMfmaDepth; ++d) {
+  for (int d = 0; d < DEPTH; ++d) {
     uint64_t ko = kbeg + (uint64_t)d * 64 + 16 * lg;
     ko = ko < klast ? ko : klast;
 #pragma unroll
@@ -307,7 +313,7 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
   }
   __syncthreads();
 
-  constexpr int kChunksPerTurn = kMfmaDepth / kMfmaChunkSteps;  // one turn of the A ring
+  constexpr int kChunksPerTurn = DEPTH / kMfmaChunkSteps;  // one turn of the A ring
   for (uint32_t c = 0; c < nchunks; c += kChunksPerTurn) {
     // a whole ring turn per iteration so that every ring slot index is static
 #pragma unroll
@@ -330,7 +336,7 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
 #pragma unroll
         for (int s = 0; s < kMfmaChunkSteps; ++s) {
           const uint32_t step = cc * kMfmaChunkSteps + s;
-          const int slot = (half * kMfmaChunkSteps + s) % kMfmaDepth;
+          const int slot = (half * kMfmaChunkSteps + s) % DEPTH;
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
             const v4i bf = bl[(s * 4 + lg) * DCOLS + ct * 16 + li];
@@ -345,7 +351,7 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
             // refill re-reads the last step (valid, unused): keeping it
             // unconditional keeps the chunk one basic block, so the compiler
             // cannot sink the digit-chunk loads down to their LDS store.
-            uint32_t nxt = step - 1 + kMfmaDepth;
+            uint32_t nxt = step - 1 + DEPTH;
             nxt = nxt < nsteps ? nxt : nsteps - 2;
             uint64_t ko0 = kbeg + (uint64_t)nxt * 64 + 16 * lg;
             uint64_t ko1 = ko0 + 64;
@@ -500,7 +506,7 @@ bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPl
     p->part_bytes = p->nkb > 1 ? p->nkb * M * 4 : 0;
   } else {
     p->mfma = true;
-    p->bgroup = B < 32 ? B : 32;
+    p->bgroup = B < kMfmaMaxCols ? B : kMfmaMaxCols;
     p->bpad = (uint32_t)align_up(p->bgroup, 16);
     p->kblock = K > kMfmaKBlockMax ? kMfmaKBlockMax : align_up(K, kMfmaChunkK);
     p->nkb = ceil_div(K, p->kblock);
@@ -557,8 +563,12 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint32_t* dst = pl.nkb > 1 ? part : out;
     timer_mark_start(stream);  // first pass only
-    if (bpad == 16) e = launch_mfma<4>(db, dig, dst, M, K, pl, bg, B, c0, stream);
-    else e = launch_mfma<8>(db, dig, dst, M, K, pl, bg, B, c0, stream);
+    switch (bpad) {
+      case 16: e = launch_mfma<4>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+      case 32: e = launch_mfma<8>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+      case 48: e = launch_mfma<12>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+      default: e = launch_mfma<16>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+    }
     if (e != hipSuccess) return e;
     if (c0 + pl.bgroup >= B) timer_mark_stop(stream);  // last pass: before its reduction
     if (pl.nkb > 1) {

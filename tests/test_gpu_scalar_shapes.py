@@ -27,7 +27,7 @@ N_LWE = 1280
 
 
 @pytest.mark.parametrize("M,K,B", [(100, 4096, N_LWE), (37, 1040, N_LWE + 1), (300, 16400, 96),
-                                   (65, 2048, 33)])
+                                   (65, 2048, 33), (77, 4160, 64), (100, 2048, 65), (260, 20480, 48)])
 def test_wide_query_full(M, K, B):
     import torch
 
