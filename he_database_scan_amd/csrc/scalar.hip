@@ -20,8 +20,8 @@
 //    128-bit loads, one v_dot4 (4 int8 products) per DB dword per digit plane.
 //    Split-K partial sums (one per row and k-block) are added mod 2^32.
 //  * B  > 1 (S3): int8 MFMA (v_mfma_i32_16x16x64_i8).  DB rows are the A
-//    operand, the 4*B digit columns the B operand; int32 accumulation never
-//    overflows because a k-block is at most 2^14 long (|sum| <= 2^28).  The
+//    operand, the 4*B digit columns the B operand; the int32 accumulators
+//    wrap modulo 2^32, which is exact for a result taken mod 2^32.  The
 //    epilogue recombines the four digit planes with shifts, mod 2^32.
 #include <hip/hip_runtime.h>
 
@@ -35,7 +35,12 @@ constexpr int kGemvJ = 4;                          // 16-byte loads per lane per
 constexpr uint64_t kGemvKBlock = 64 * 16 * kGemvJ;  // 4096
 constexpr int kGemvRowsPerWave = 64;
 constexpr int kGemvRowBatch = 4;
-constexpr uint64_t kMfmaKBlockMax = 16384;
+// The B > 1 path splits K only as far as it must for the tiles to fill the
+// GPU (a tile is 256 rows of one k-block): int8 MFMA accumulation wraps
+// modulo 2^32 in two's complement (measured on gfx950 with sums well past
+// 2^31), so a k-block of any length gives the exact digit-plane sums mod
+// 2^32, which is all the recombination below needs.
+constexpr uint64_t kMfmaTargetTiles = 512;
 constexpr uint32_t kMfmaMaxCols = 64;  // query columns per MFMA pass (4 digit planes each)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -508,7 +513,11 @@ bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPl
     p->mfma = true;
     p->bgroup = B < kMfmaMaxCols ? B : kMfmaMaxCols;
     p->bpad = (uint32_t)align_up(p->bgroup, 16);
-    p->kblock = K > kMfmaKBlockMax ? kMfmaKBlockMax : align_up(K, kMfmaChunkK);
+    const uint64_t row_blocks = ceil_div(M, (uint64_t)kMfmaWaves * 16 * kMfmaRowTiles2);
+    uint64_t nkb = ceil_div(kMfmaTargetTiles, row_blocks);
+    const uint64_t chunks = ceil_div(K, kMfmaChunkK);
+    if (nkb > chunks) nkb = chunks;
+    p->kblock = align_up(ceil_div(K, nkb), kMfmaChunkK);
     p->nkb = ceil_div(K, p->kblock);
     p->kpad = p->nkb * p->kblock;
     p->digit_bytes = p->kpad * 4 * p->bpad;

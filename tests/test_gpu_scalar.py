@@ -126,3 +126,25 @@ def test_scalar_1gib_sampled():
 def test_scalar_64gib_sampled():
     M = K = 262144
     full_size_sampled(5, M, K, [1, 32], [0, 1, 63, 64, 131072, 200001, 262143])
+
+
+@pytest.mark.parametrize("B", [8, 32])
+def test_int32_digit_sums_wrap_inside_one_k_block(B):
+    """131072 rows x 2^17: the plan keeps K in one block (enough row tiles),
+    so each digit-plane sum of (-128)*(-128) products reaches 2^31 inside a
+    single int32 accumulator.  Q = 0x80808080 has digits (-128, -127, -127,
+    -127); out = K * (-128) * 0x80808080 mod 2^32 for every element."""
+    import torch
+
+    M = K = 1 << 17
+    say(f"scalar wrap M={M} K={K} B={B}")
+    d_db = torch.full((M, K), -128, dtype=torch.int8, device="cuda:0")
+    d_q = torch.full((K, B), 0x80808080 - (1 << 32), dtype=torch.int32, device="cuda:0")
+    d_o = empty_u32((M, B))
+    ws = torch.empty(pirscan.scalar_workspace_bytes(M, K, B), dtype=torch.uint8, device="cuda:0")
+    pirscan.scalar_gemm_u32(d_db, d_q, d_o, ws)
+    want = (K * -128 * 0x80808080) % (1 << 32)
+    want_i32 = want - (1 << 32) if want >= (1 << 31) else want
+    assert bool((d_o == want_i32).all())
+    del d_db, d_q, d_o, ws
+    release()
