@@ -100,8 +100,13 @@ def test_scalar_workspace_sizes():
     # B=1: 4 digit bytes per k (k padded to 4096) + split-K partials
     assert pirscan.scalar_workspace_bytes(32768, 32768, 1) == 32768 * 4 + 8 * 32768 * 4
     assert pirscan.scalar_workspace_bytes(10, 4096, 1) == 4096 * 4          # one k-block: no partials
-    # B=8 (one MFMA pass, 16 padded digit columns x 4 planes)
-    assert pirscan.scalar_workspace_bytes(32768, 32768, 8) == 32768 * 64 + 2 * 32768 * 8 * 4
+    # B=8 (one MFMA pass, 16 padded digit columns x 4 planes); K splits into as
+    # many blocks as it takes to reach 512 tiles of 256 rows: 128 row tiles -> 4
+    assert pirscan.scalar_workspace_bytes(32768, 32768, 8) == 32768 * 64 + 4 * 32768 * 8 * 4
+    # enough row tiles: one k-block, no partial sums (the 64 GiB B=32 shape)
+    assert pirscan.scalar_workspace_bytes(262144, 262144, 32) == 262144 * 128
+    # B=1280: passes of 64 columns, digit planes for one pass
+    assert pirscan.scalar_workspace_bytes(1 << 20, 1 << 16, 1280) == (1 << 16) * 256
     assert pirscan.scalar_workspace_bytes(0, 16, 1) == 0
     assert pirscan.scalar_workspace_bytes(5, 17, 1) == 0                    # generic path
 
