@@ -87,11 +87,11 @@ _CSRC = os.path.join(ROOT, "he_database_scan_amd", "csrc")
 # The source file of each scan's main kernel (traffic figures are dropped once
 # that file changes).
 KERNEL_SOURCES = {
-    "rowsel_48GiB_B1": os.path.join(_CSRC, "rowsel.hip"),
+    "rowsel_48GiB_B1": os.path.join(_CSRC, "rowsel_mfma.hip"),
     "rowsel_48GiB_B16": os.path.join(_CSRC, "rowsel_mfma.hip"),
     "scalar_64GiB_B1": os.path.join(_CSRC, "scalar.hip"),
     "scalar_64GiB_B32": os.path.join(_CSRC, "scalar.hip"),
-    "exppack_15GiB_B1": os.path.join(_CSRC, "rowsel.hip"),
+    "exppack_15GiB_B1": os.path.join(_CSRC, "rowsel_mfma.hip"),
     "exppack_15GiB_B16": os.path.join(_CSRC, "rowsel_mfma.hip"),
     **{name: os.path.join(_CSRC, "scalar.hip") for name in SHAPE_SCANS},
     "ntt_rns_fwd_hint": os.path.join(_CSRC, "ntt.hip"),
@@ -124,7 +124,7 @@ class Workloads:
         log("setup: RowSel 48 GiB DB (synthesise p-major, one-time relayout)")
         db = torch.empty((RS_D0, RS_D1, P), dtype=torch.int32, device=dev)
         synth.fill_residues_(db, SEEDS["rowsel"], synth.STREAM_ROWSEL_DB, RS_N, RS_Q)
-        self.dbt = torch.empty((P, RS_D0, RS_D1), dtype=torch.int32, device=dev)
+        self.dbt = torch.empty(pirscan.layout_db_bytes(self.shape), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         pirscan.layout_db(self.shape, db, self.dbt)
@@ -153,7 +153,7 @@ class Workloads:
         self.eshape = pirscan.ExppackShape.make(RS_N, RS_Q, EP_DR, EP_N)
         h = torch.empty((EP_DR, EP_N, P), dtype=torch.int32, device=dev)
         synth.fill_residues_(h, SEEDS["exppack"], synth.STREAM_EXPPACK_H, RS_N, RS_Q)
-        self.ht = torch.empty((P, EP_N, EP_DR), dtype=torch.int32, device=dev)
+        self.ht = torch.empty(pirscan.exppack_layout_h_bytes(self.eshape), dtype=torch.uint8, device=dev)
         pirscan.exppack_layout_h(self.eshape, h, self.ht)
         torch.cuda.synchronize()
         del h
@@ -260,9 +260,10 @@ class Workloads:
 
 
 # int8 MACs the MFMA paths issue per algorithmic MAC: the scalar B>1 GEMM
-# multiplies 4 query digit planes; batched RowSel / ExpPack multiply 4 x 4
-# limb pairs.
-MFMA_MACS_PER_MAC = {"rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4, "exppack_15GiB_B16": 16,
+# multiplies 4 query digit planes; RowSel / ExpPack multiply 4 x 4 limb pairs,
+# and at m = 2 pad the 2 rows to a 16-row tile (x 8).
+MFMA_MACS_PER_MAC = {"rowsel_48GiB_B1": 128, "rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4,
+                     "exppack_15GiB_B1": 128, "exppack_15GiB_B16": 16,
                      **{name: 4 for name, (M, K, B) in SHAPE_SCANS.items() if B > 1}}
 # shapes whose int8 MFMA work exceeds what HBM time allows: priced against the MFMA peak
 MFMA_BOUND = {"scalar_hint_64GiB_n1280", "scalar_fold2_4GiB_n1281"}
@@ -314,12 +315,12 @@ def traffic_for(name):
 # size, and the scans are told apart by the (kernel, grid) group that appears
 # first in dispatch order.
 SCAN_KERNELS = {
-    "rowsel_48GiB_B1": "rowsel_kernel<2,",
-    "rowsel_48GiB_B16": "rowsel_mfma_kernel<2, 2",
+    "rowsel_48GiB_B1": "rowsel_packed_direct_kernel<1>",
+    "rowsel_48GiB_B16": "rowsel_packed_kernel<2, 2",
     "scalar_64GiB_B1": "gemv_kernel",
     "scalar_64GiB_B32": "mfma_kernel<8>",
-    "exppack_15GiB_B1": "rowsel_kernel<2,",
-    "exppack_15GiB_B16": "rowsel_mfma_kernel<2, 2",
+    "exppack_15GiB_B1": "rowsel_packed_direct_kernel<1>",
+    "exppack_15GiB_B16": "rowsel_packed_kernel<2, 2",
     **{name: ("gemv_kernel" if B == 1 else "mfma_kernel<8>") for name, (M, K, B) in SHAPE_SCANS.items()},
     "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
     "ntt_inv_hint": "ntt_kernel<12, true>",

@@ -29,7 +29,7 @@ struct LimbConsts {
 // Z on the way.
 struct RowselLaunch {
   const uint32_t* ct;
-  const uint32_t* dbt;     // [P][D0][D1]
+  const uint32_t* dbt;     // [P][D0][D1], or the packed fragments (launch_rowsel_packed)
   uint32_t* out;
   uint32_t* out_t;         // staging [P][m][D1] (workspace)
   const uint32_t* add;     // optional body term (residues < q), null for none
@@ -74,12 +74,41 @@ hipError_t launch_rowsel(const RowselLaunch& a, void* workspace, hipStream_t str
 // out_t [P][m][D1] -> out (strided, p-major), adding the body term if any.
 hipError_t launch_out_relayout(const RowselLaunch& a, const uint32_t* out_t, hipStream_t stream);
 
-// Batched RowSel on int8 MFMA: m >= kRowselMfmaMinRows, every q < 2^31,
-// D0 <= 16384, D0*D1 < 2^31.  Needs a workspace of rowsel_mfma_workspace_bytes().
-constexpr uint32_t kRowselMfmaMinRows = 16;
-bool rowsel_mfma_eligible(const RowselLaunch& a, uint32_t R);
-size_t rowsel_mfma_workspace_bytes(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1);
-hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace, hipStream_t stream);
+// RowSel / ExpPack on int8 MFMA over centred signed limbs, any m, with the
+// DB operand packed once into B-fragment order.  Usable when every q < 2^31
+// and D0 <= kPackedMaxD0 (the int32 limb diagonals cannot overflow); other
+// shapes keep the [P][D0][D1] layout and the VALU scan.
+constexpr uint32_t kPackedMaxD0 = 16384;
+bool rowsel_packed_ok(const uint32_t* q, uint32_t R, uint32_t D0);
+// Bytes of the packed operand: per point ceil(D1/16) x ceil(D0/64) x 4 KiB.
+uint64_t packed_layout_bytes(uint64_t P, uint32_t D0, uint32_t D1);
+
+// Limb packing of a p-major operand into MFMA fragments.  Source word
+// (row, k, p) at src[row * s_row + k * s_k + p] (rows row_base .. rows-1,
+// k < K); the 16 bytes of fragment lane (li, lg) of (p, t, s, limb j) at
+// dst[p * d_p + t * d_t + s * d_s + (4 j + lg) * lpg + li] (strides in
+// 16-byte units) for li < lpg, holding limb j of the centred residues of row
+// row_base + 16t + li at k = 64s + 16lg + 0..15; zero past rows / K.  With
+// lpg = 16 a fragment is 1 KiB of contiguous lanes.
+struct PackDesc {
+  const uint32_t* src;
+  void* dst;
+  uint64_t P, s_row, s_k;
+  uint64_t d_p, d_t, d_s;
+  uint32_t N, rows, row_base, K, tiles, S;
+  uint32_t lpg;  // lanes stored per k-group (16, or the live rows of a small batch)
+  uint32_t q[kMaxLimbs];
+};
+hipError_t launch_pack(const PackDesc& d, hipStream_t stream);
+// The one-time DB / hint packing: rows = the DB's columns (D1), K = D0,
+// tile-major fragments [p][t][s][j][lane].
+hipError_t launch_pack_operand(const uint32_t* src, void* dst, uint64_t P, uint32_t N, const uint32_t* q,
+                               uint32_t R, uint32_t rows, uint32_t K, uint64_t s_row, uint64_t s_k,
+                               hipStream_t stream);
+// The scan (a.dbt = the packed operand).  Workspace: the A fragments of one
+// 32-row pass plus the per-point output staging.
+size_t rowsel_packed_workspace_bytes(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1);
+hipError_t launch_rowsel_packed(const RowselLaunch& a, uint32_t R, void* workspace, hipStream_t stream);
 
 // Products of (q-1)^2 that fit between folds for modulus q (host helper).
 uint32_t rowsel_fold_period(uint32_t q);

@@ -72,7 +72,12 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Validates a RowSel shape; on success returns P and the DB word count.
+// Bytes of the packed operand, with the same overflow bound as the words.
+unsigned __int128 packed_bytes_wide(unsigned __int128 P, uint32_t D0, uint32_t D1) {
+  return P * ((D1 + 15ull) / 16) * ((D0 + 63ull) / 64) * 4096;
+}
+
+// Validates a RowSel shape; on success returns P and the p-major DB word count.
 bool rowsel_shape_ok(const pirscan_rowsel_shape* s, uint64_t* P, uint64_t* db_words) {
   if (!s || s->N == 0 || s->R == 0 || s->R > PIRSCAN_MAX_R || s->D0 == 0 || s->D1 == 0) return false;
   for (uint32_t r = 0; r < s->R; ++r)
@@ -80,6 +85,7 @@ bool rowsel_shape_ok(const pirscan_rowsel_shape* s, uint64_t* P, uint64_t* db_wo
   const unsigned __int128 p = (unsigned __int128)s->R * s->N;
   const unsigned __int128 words = p * s->D0 * s->D1;
   if (words * 4 > (unsigned __int128)(~(uint64_t)0 >> 1)) return false;
+  if (packed_bytes_wide(p, s->D0, s->D1) > (unsigned __int128)(~(uint64_t)0 >> 1)) return false;
   *P = (uint64_t)p;
   *db_words = (uint64_t)words;
   return true;
@@ -111,6 +117,7 @@ bool exppack_shape_ok(const pirscan_exppack_shape* s, uint32_t B, uint64_t* P, u
   const unsigned __int128 h = p * s->Dr * s->n, c = p * s->n * 2 * B, g = p * s->Dr * B,
                           o = p * s->Dr * 2 * B;
   if (h * 4 > kMaxBytes || c * 4 > kMaxBytes || o * 4 > kMaxBytes) return false;
+  if (packed_bytes_wide(p, s->n, s->Dr) > kMaxBytes) return false;
   *P = (uint64_t)p;
   *h_words = (uint64_t)h;
   *c_words = (uint64_t)c;
@@ -144,11 +151,20 @@ void exppack_launch_desc(const pirscan_exppack_shape* s, uint32_t B, uint64_t P,
   fill_limb_consts(s->q, s->R, a);
 }
 
-// Workspace of the point-wise modular GEMM: the MFMA path's relayouts, or the
-// VALU path's per-point output staging.
+// Whether the shape's DB / hint operand is packed for the MFMA scan (every
+// q < 2^31 and D0 <= 16384), or kept word-transposed for the VALU scan.
+bool packed_shape(const uint32_t* q, uint32_t R, uint32_t D0) { return pirscan::rowsel_packed_ok(q, R, D0); }
+
+// Bytes of the relaid DB / hint operand (D0 = reduction extent, D1 = columns).
+uint64_t operand_layout_bytes(const uint32_t* q, uint32_t R, uint64_t P, uint32_t D0, uint32_t D1) {
+  if (packed_shape(q, R, D0)) return pirscan::packed_layout_bytes(P, D0, D1);
+  return 4ull * P * D0 * D1;
+}
+
+// Workspace of the point-wise modular GEMM: the MFMA path's A fragments and
+// output staging, or the VALU path's output staging.
 size_t modgemm_workspace_bytes(const pirscan::RowselLaunch& a, uint32_t R) {
-  if (pirscan::rowsel_mfma_eligible(a, R))
-    return pirscan::rowsel_mfma_workspace_bytes(a.P, a.m, a.D0, a.D1);
+  if (packed_shape(a.lc.q, R, a.D0)) return pirscan::rowsel_packed_workspace_bytes(a.P, a.m, a.D0, a.D1);
   return pirscan::rowsel_valu_workspace_bytes(a.P, a.m, a.D1);
 }
 
@@ -165,10 +181,11 @@ int run_modgemm(const pirscan::RowselLaunch& a, uint32_t R, const Span* bufs, in
     return PIRSCAN_EINVAL;
   for (int i = 0; i < nbufs; ++i)
     if (overlap(workspace, need, bufs[i].p, bufs[i].bytes)) return PIRSCAN_EINVAL;
+  const bool packed = packed_shape(a.lc.q, R, a.D0);
+  if (packed && (reinterpret_cast<uintptr_t>(a.dbt) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
-  if (pirscan::rowsel_mfma_eligible(a, R))
-    return device_status(pirscan::launch_rowsel_mfma(a, R, workspace, (hipStream_t)stream));
+  if (packed) return device_status(pirscan::launch_rowsel_packed(a, R, workspace, (hipStream_t)stream));
   return device_status(pirscan::launch_rowsel(a, workspace, (hipStream_t)stream));
 }
 
@@ -278,16 +295,22 @@ extern "C" {
 size_t pirscan_layout_db_bytes(const pirscan_rowsel_shape* s) {
   uint64_t P = 0, words = 0;
   if (!rowsel_shape_ok(s, &P, &words)) return 0;
-  return (size_t)(words * 4);
+  return (size_t)operand_layout_bytes(s->q, s->R, P, s->D0, s->D1);
 }
 
 int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor, uint32_t* db_tiled,
                       void* stream) {
   uint64_t P = 0, words = 0;
   if (!rowsel_shape_ok(s, &P, &words) || !db_pmajor || !db_tiled) return PIRSCAN_EINVAL;
-  if (overlap(db_pmajor, words * 4, db_tiled, words * 4)) return PIRSCAN_EINVAL;
+  const uint64_t tiled_bytes = operand_layout_bytes(s->q, s->R, P, s->D0, s->D1);
+  const bool packed = packed_shape(s->q, s->R, s->D0);
+  if (overlap(db_pmajor, words * 4, db_tiled, tiled_bytes)) return PIRSCAN_EINVAL;
+  if (packed && (reinterpret_cast<uintptr_t>(db_tiled) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
+  if (packed)  // [D0][D1][P]: column n is fragment row n (stride P), k has stride D1*P
+    return device_status(pirscan::launch_pack_operand(db_pmajor, db_tiled, P, s->N, s->q, s->R, s->D1, s->D0, P,
+                                                      (uint64_t)s->D1 * P, (hipStream_t)stream));
   return device_status(pirscan::launch_layout_db(db_pmajor, db_tiled, (uint64_t)s->D0 * s->D1, P,
                                                  (hipStream_t)stream));
 }
@@ -336,24 +359,33 @@ int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint
   uint64_t dbw = 0, ctw = 0, ow = 0;
   if (!ct || !db_tiled || !out || !rowsel_launch_desc(s, m, ct, db_tiled, out, &a, &dbw, &ctw, &ow))
     return PIRSCAN_EINVAL;
-  if (overlap(out, ow * 4, ct, ctw * 4) || overlap(out, ow * 4, db_tiled, dbw * 4)) return PIRSCAN_EINVAL;
-  const Span ins[] = {{ct, ctw * 4}, {db_tiled, dbw * 4}, {out, ow * 4}};
+  const uint64_t db_bytes = operand_layout_bytes(s->q, s->R, a.P, s->D0, s->D1);
+  if (overlap(out, ow * 4, ct, ctw * 4) || overlap(out, ow * 4, db_tiled, db_bytes)) return PIRSCAN_EINVAL;
+  const Span ins[] = {{ct, ctw * 4}, {db_tiled, db_bytes}, {out, ow * 4}};
   return run_modgemm(a, s->R, ins, 3, workspace, workspace_bytes, stream);
 }
 
 size_t pirscan_exppack_layout_h_bytes(const pirscan_exppack_shape* s) {
   uint64_t P, h, c, g, o;
   if (!exppack_shape_ok(s, 0, &P, &h, &c, &g, &o)) return 0;
-  return (size_t)(h * 4);
+  return (size_t)operand_layout_bytes(s->q, s->R, P, s->n, s->Dr);
 }
 
 int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_pmajor,
                              uint32_t* h_tiled, void* stream) {
   uint64_t P, h, c, g, o;
   if (!exppack_shape_ok(s, 0, &P, &h, &c, &g, &o) || !h_pmajor || !h_tiled) return PIRSCAN_EINVAL;
-  if (overlap(h_pmajor, h * 4, h_tiled, h * 4)) return PIRSCAN_EINVAL;
+  const uint64_t tiled_bytes = operand_layout_bytes(s->q, s->R, P, s->n, s->Dr);
+  const bool packed = packed_shape(s->q, s->R, s->n);
+  if (overlap(h_pmajor, h * 4, h_tiled, tiled_bytes)) return PIRSCAN_EINVAL;
+  if (packed && (reinterpret_cast<uintptr_t>(h_tiled) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
+  // The GEMM's DB operand is H^T: hint column i is the reduction index k and
+  // row r the output column.  H [Dr][n][P]: r has stride n*P, i stride P.
+  if (packed)
+    return device_status(pirscan::launch_pack_operand(h_pmajor, h_tiled, P, s->N, s->q, s->R, s->Dr, s->n,
+                                                      (uint64_t)s->n * P, P, (hipStream_t)stream));
   // [Dr][n][P] -> [P][n][Dr]: for each hint column i, a Dr x P transpose.
   pirscan::TransposeDesc t{};
   t.src = h_pmajor;
@@ -383,12 +415,12 @@ int pirscan_exppack_modgemm(const pirscan_exppack_shape* s, uint32_t B, const ui
   if (B == 0 || !C || !h_tiled || !out || !exppack_shape_ok(s, B, &P, &hw, &cw, &gw, &ow))
     return PIRSCAN_EINVAL;
   const uint64_t gb = G ? gw * 4 : 0;
-  if (overlap(out, ow * 4, C, cw * 4) || overlap(out, ow * 4, h_tiled, hw * 4) ||
-      overlap(out, ow * 4, G, gb))
+  const uint64_t hb = operand_layout_bytes(s->q, s->R, P, s->n, s->Dr);
+  if (overlap(out, ow * 4, C, cw * 4) || overlap(out, ow * 4, h_tiled, hb) || overlap(out, ow * 4, G, gb))
     return PIRSCAN_EINVAL;
   pirscan::RowselLaunch a;
   exppack_launch_desc(s, B, P, C, h_tiled, G, out, &a);
-  const Span ins[] = {{C, cw * 4}, {h_tiled, hw * 4}, {G, gb}, {out, ow * 4}};
+  const Span ins[] = {{C, cw * 4}, {h_tiled, hb}, {G, gb}, {out, ow * 4}};
   return run_modgemm(a, s->R, ins, 4, workspace, workspace_bytes, stream);
 }
 

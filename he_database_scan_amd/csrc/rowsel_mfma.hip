@@ -1,18 +1,18 @@
-// rowsel_mfma.hip -- batched RowSel on int8 MFMA (gfx950).
+// rowsel_mfma.hip -- RowSel and ExpPack on int8 MFMA over centred signed
+// limbs (gfx950), for every batch size.
 //
-// For a batch of m >= 16 ciphertext polynomials the per-point product
-// C[mi][n] = sum_k A[mi][k] * B[k][n] (A = ct, B = DB, all values < q) is a
-// dense contraction, so it runs on v_mfma_i32_16x16x64_i8 instead of the
-// 32x32->64-bit VALU multiply (GPIR: "Enabling Practical Private Information
-// Retrieval with GPUs" observes that batching raises RowSel's arithmetic
-// intensity; VIPIR section 4.1 emulates a wide integer product with INT8
-// tensor-core GEMMs on split operands and section 4.2 discusses the modular
-// GEMM's reduction overhead).
+// The per-point product C[mi][n] = sum_k A[mi][k] * B[k][n] (A = ct, B = DB,
+// all values < q) runs on v_mfma_i32_16x16x64_i8 (VIPIR section 4.1 emulates
+// a wide integer product with INT8 tensor-core GEMMs on split operands,
+// section 4.2 discusses the modular GEMM's reduction; GPIR: "Enabling
+// Practical Private Information Retrieval with GPUs" observes that batching
+// raises RowSel's arithmetic intensity).  At batch 1 the matrix cores are
+// mostly idle, but the scan is HBM-bound at every batch and the MFMA form
+// needs no per-word ALU work, so one kernel serves all m.
 //
-// Every value x < q is first centred, v = x - q if x > q/2 (so |v| <= q/2 <
-// 2^30 when q < 2^31), then written in four signed 8-bit limbs
-// v = sum_i v_i 2^(8i), v_i in [-128, 127] (the bytes of
-// (v + 0x80808080) ^ 0x80808080).  Then
+// Every value x < q is centred, v = x - q if x > q/2 (so |v| <= q/2 < 2^30
+// for q < 2^31), and written in four signed 8-bit limbs v = sum_i v_i 2^(8i),
+// v_i in [-128, 127] (the bytes of (v + 0x80808080) ^ 0x80808080).  Then
 //
 //   sum_k a_k b_k = sum_{d=0..6} 2^(8d) S_d,  S_d = sum_{i+j=d} sum_k a_{k,i} b_{k,j}
 //
@@ -23,22 +23,23 @@
 // fold as the VALU scan, and one Barrett reduction.
 //
 // Data movement:
-//  * ct is relaid per query (two small passes into the caller's workspace):
-//    a strided transpose to [p][mi][k] (from RowSel's [mi][k][p] or ExpPack's
-//    C [k][mi][p]) and a limb split into MFMA A-fragment order, so
-//    each wavefront loads its A fragments as 16-byte vectors.
-//  * The DB stays in the scan layout [p][k][n].  Lane (li, lg) of a B fragment
-//    needs 16 consecutive k of its column; the two column tiles of a wave take
-//    the even and the odd columns of a 32-column block, so the lane's two
-//    columns are adjacent and each k comes in one 64-bit load (an instruction
-//    covers 128-byte runs of 4 k-rows), addressed by 32-bit offsets from the
-//    point's wave-uniform base.  The words are centred and split into the four
-//    limb fragments in registers (4 ALU ops per word, and a byte transpose of
-//    8 byte-permutes per 4 words).
-//  * Results are written per point, [p][mi][n] (contiguous 64-byte runs), and
-//    a transpose pass produces the p-major output (adding ExpPack's body term
-//    G where the launch carries one).
+//  * The DB (or ExpPack's hint) is packed once, at layout time, into MFMA
+//    B-fragment order: per point, per 16-column tile t and 64-k step s, four
+//    1 KiB fragments (one per limb), lane (li, lg) holding limb j of the 16
+//    consecutive k 64s + 16lg + 0..15 of column 16t + li.  A tile's steps are
+//    contiguous, so a wavefront streams its columns as 1 KiB vector loads with
+//    no ALU work per word.
+//  * The query side (ct, or ExpPack's C) is packed per call the same way into
+//    A fragments [p][s][row tile][limb][lane] in the workspace.  The four
+//    wavefronts of a workgroup scan the same point, so each step's A
+//    fragments come into LDS once per workgroup (direct global-to-LDS loads,
+//    a three-step ring) and every wave reads them from there.
+//  * Results are written per point, [p][mi][n], and a transpose pass
+//    produces the p-major output (adding ExpPack's body term G where the
+//    launch carries one).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.hpp"
 
@@ -47,6 +48,9 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
+constexpr int kRing = 3;         // A-fragment ring depth in steps
+constexpr uint32_t kDirectRows = 16;  // passes of at most this many rows: the direct kernel
+constexpr uint32_t kFrag = 256;  // v4i per step and 16-row (or 16-column) tile: 4 limbs x 64 lanes
 
 // Centred signed-limb digits of a residue x < q (the byte vector of the
 // centred value's four signed 8-bit digits): with v = x - q when x > q/2,
@@ -84,197 +88,121 @@ __device__ __forceinline__ void limb_fragments(const uint32_t w[16], v4i f[4]) {
   }
 }
 
-// ct_t [P][m][D0] -> A fragments [p][s][mt][limb][lane] (16 bytes each) for
-// rows m_base .. m_base + 16*MT of this pass; zero past m and past D0.
-__global__ __launch_bounds__(kThreads) void rowsel_limbs_kernel(const uint32_t* __restrict__ ct_t,
-                                                                v4i* __restrict__ limbs, uint64_t P,
-                                                                uint32_t m, uint32_t D0, uint32_t m_base,
-                                                                uint32_t MT, uint32_t S, uint32_t N,
-                                                                LimbConsts lc) {
-  const uint64_t total = P * S * MT * 64;
+// ---------------------------------------------------------------------------
+// Limb packing: a p-major operand -> MFMA fragments.
+// Source word (row, k, p) at src[row * s_row + k * s_k + p] for rows
+// row_base .. rows-1 and k < K; fragment lane (li, lg) of (p, t, s, j) at
+// dst[p * d_p + t * d_t + s * d_s + (4 j + lg) * lpg + li] for li < lpg,
+// holding limb j of row row_base + 16t + li at k = 64s + 16lg + 0..15 (with
+// lpg = 16 that is j * 64 + lane, whole 1 KiB fragments).  Rows past `rows`
+// and k past K give zero bytes.
+// ---------------------------------------------------------------------------
+
+// One workgroup per (32 points, k-group lg, tile t, step s): the tile's 16
+// rows x 16 k are read as 256 runs of 32 points (128 contiguous bytes each)
+// into LDS, then each thread forms the fragment lanes of points p: 16 words
+// -> centred signed limbs -> 4 x 16 bytes.  Needs P % 4 == 0, a 16-byte
+// aligned source and strides that are multiples of 4 words.
+// LDS word of (row r, point p): r*32 + ((p + 4*(r/16)) mod 32), which keeps
+// both the 16-byte row stores and the per-thread column reads at two-way
+// bank conflicts at most.
+constexpr int kPackPoints = 32;
+__global__ __launch_bounds__(kThreads) void pack_limbs4_kernel(PackDesc d, uint64_t pblocks, uint64_t total) {
+  __shared__ uint32_t tile[256 * kPackPoints];
+  const uint32_t tid = threadIdx.x;
+  for (uint64_t id = blockIdx.x; id < total; id += gridDim.x) {
+    const uint64_t pb = id % pblocks;
+    uint64_t rest = id / pblocks;
+    const uint32_t lg = (uint32_t)(rest % 4);
+    rest /= 4;
+    const uint32_t t = (uint32_t)(rest % d.tiles);
+    const uint32_t s = (uint32_t)(rest / d.tiles);
+    const uint64_t p0 = pb * kPackPoints;
+    __syncthreads();  // the previous item's reads of `tile` are done
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+      const uint32_t r = pass * 32 + tid / 8, c4 = (tid % 8) * 4;
+      const uint64_t row = (uint64_t)d.row_base + t * 16 + r / 16;
+      const uint32_t k = s * 64 + lg * 16 + r % 16;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < d.rows && k < d.K && p0 + c4 < d.P)
+        v = *reinterpret_cast<const uint4*>(d.src + row * d.s_row + (uint64_t)k * d.s_k + p0 + c4);
+      *reinterpret_cast<uint4*>(&tile[r * kPackPoints + ((c4 + 4 * (r / 16)) % kPackPoints)]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t li = tid % 16, pp = h * 16 + tid / 16;
+      const uint64_t p = p0 + pp;
+      if (p >= d.P || li >= d.lpg) continue;
+      const uint32_t q = d.q[p / d.N], half = q / 2;
+      uint32_t w[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        w[i] = centred_digits(tile[(li * 16 + i) * kPackPoints + ((pp + 4 * li) % kPackPoints)], half,
+                              0x80808080u, 0x80808080u - q);  // x = 0 gives digit bytes 0
+      v4i f[4];
+      limb_fragments(w, f);
+      v4i* dst = static_cast<v4i*>(d.dst) + p * d.d_p + t * d.d_t + s * d.d_s + lg * d.lpg + li;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j * 4 * d.lpg] = f[j];
+    }
+  }
+}
+
+// Any P, strides and alignment: one thread per fragment lane, 16 strided loads.
+__global__ __launch_bounds__(kThreads) void pack_limbs_kernel(PackDesc d, uint64_t total) {
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t e = (uint64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
     const uint32_t lane = (uint32_t)(e % 64);
     uint64_t rest = e / 64;
-    const uint32_t mt = (uint32_t)(rest % MT);
-    rest /= MT;
-    const uint32_t s = (uint32_t)(rest % S);
-    const uint64_t p = rest / S;
+    const uint32_t s = (uint32_t)(rest % d.S);
+    rest /= d.S;
+    const uint32_t t = (uint32_t)(rest % d.tiles);
+    const uint64_t p = rest / d.tiles;
     const uint32_t li = lane % 16, lg = lane / 16;
-    const uint32_t mi = m_base + mt * 16 + li;
-    const uint32_t q = lc.q[p / N], half = q / 2;
+    if (li >= d.lpg) continue;
+    const uint64_t row = (uint64_t)d.row_base + t * 16 + li;
+    const uint32_t q = d.q[p / d.N], half = q / 2;
     uint32_t w[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint32_t k = s * 64 + lg * 16 + t;
-      const uint32_t x = (mi < m && k < D0) ? ct_t[(p * m + mi) * D0 + k] : 0u;
-      w[t] = centred_digits(x, half, 0x80808080u, 0x80808080u - q);  // x = 0 gives digit bytes 0
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t k = s * 64 + lg * 16 + i;
+      const uint32_t x = (row < d.rows && k < d.K) ? d.src[row * d.s_row + (uint64_t)k * d.s_k + p] : 0u;
+      w[i] = centred_digits(x, half, 0x80808080u, 0x80808080u - q);
     }
     v4i f[4];
     limb_fragments(w, f);
+    v4i* dst = static_cast<v4i*>(d.dst) + p * d.d_p + t * d.d_t + s * d.d_s + lg * d.lpg + li;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) limbs[((((p * S + s) * MT + mt) * 4 + j) * 64) + lane] = f[j];
+    for (int j = 0; j < 4; ++j) dst[j * 4 * d.lpg] = f[j];
   }
 }
 
-// ct(mi, k, p) -> A fragments [p][s][mt][limb][lane] in one pass, for rows
-// m_base .. m_base + 16*MT: one workgroup per (32 points, step s, row tile
-// mt, k-group lg).  The 16 rows x 16 k of the tile are read as 256 runs of
-// 32 points (128 contiguous bytes each) into LDS, then each thread forms the
-// fragment lanes (li, lg) of points p: 16 words (k = 64 s + 16 lg + t) ->
-// centred signed limbs -> 4 x 16 bytes, written as 256-byte runs per point
-// and limb.  Rows past m and k past D0 are zero.  Needs P % 4 == 0 and a
-// 16-byte aligned ct with strides that are multiples of 4 words.
-// LDS word of (row r, point p): r*32 + ((p + 4*(r/16)) mod 32), which keeps
-// both the 16-byte row stores and the per-thread column reads at two-way
-// bank conflicts at most.
-constexpr int kPrepPoints = 32;
-__global__ __launch_bounds__(kThreads) void rowsel_prep_kernel(RowselLaunch a, v4i* __restrict__ limbs,
-                                                               uint32_t m_base, uint32_t MT, uint32_t S,
-                                                               uint32_t pblocks) {
-  __shared__ uint32_t tile[256 * kPrepPoints];
-  const uint32_t tid = threadIdx.x;
-  uint32_t id = blockIdx.x;
-  const uint32_t pb = id % pblocks;
-  id /= pblocks;
-  const uint32_t lg = id % 4;
-  id /= 4;
-  const uint32_t mt = id % MT;
-  const uint32_t s = id / MT;
-  const uint64_t p0 = (uint64_t)pb * kPrepPoints;
-  // load: row r = li*16 + t (mi = m_base + 16 mt + li, k = 64 s + 16 lg + t), 8 threads x 16 B per row
-#pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const uint32_t r = pass * 32 + tid / 8, c4 = (tid % 8) * 4;
-    const uint32_t mi = m_base + mt * 16 + r / 16, k = s * 64 + lg * 16 + r % 16;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (mi < a.m && k < a.D0 && p0 + c4 < a.P)
-      v = *reinterpret_cast<const uint4*>(a.ct + mi * a.ct_sm + (uint64_t)k * a.ct_sk + p0 + c4);
-    *reinterpret_cast<uint4*>(&tile[r * kPrepPoints + ((c4 + 4 * (r / 16)) % kPrepPoints)]) = v;
-  }
-  __syncthreads();
-  // form: thread -> (li = tid % 16, point pair), two points per thread
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t li = tid % 16, pp = h * 16 + tid / 16;
-    const uint64_t p = p0 + pp;
-    if (p >= a.P) continue;
-    const uint32_t q = a.lc.q[p / a.N], half = q / 2;
-    uint32_t w[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint32_t r = li * 16 + t;
-      w[t] = centred_digits(tile[r * kPrepPoints + ((pp + 4 * li) % kPrepPoints)], half, 0x80808080u,
-                            0x80808080u - q);
-    }
-    v4i f[4];
-    limb_fragments(w, f);
-    v4i* dst = limbs + (((p * S + s) * MT + mt) * 4) * 64 + li + 16 * lg;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j * 64] = f[j];
-  }
-}
+// ---------------------------------------------------------------------------
+// The scan.
+// ---------------------------------------------------------------------------
 
 struct MfmaEpilogue {
   uint32_t w[kMaxLimbs][7];  // 2^(8d) mod q
   uint32_t corr[kMaxLimbs];  // -(2^31 * sum_d w_d) mod q: undoes the +2^31 offsets
 };
 
-// DB words of one 64-k step into w[nt][t]: 16 consecutive k (from kb) of the
-// lane's column in each tile.  CLAMP: the last step, where rows past D0 are
-// replaced by row D0-1 (the A limbs are zero there, so any valid row serves).
-// PAIR: the lane's two columns are adjacent, so both come in one 64-bit load.
-// Offsets are 32-bit words from the point's (wave-uniform) base.
-template <int NTW, bool PAIR, bool CLAMP>
-__device__ __forceinline__ void load_b_step(const uint32_t* dbp, const uint32_t (&col)[NTW], uint32_t kb,
-                                            uint32_t D0, uint32_t D1, uint32_t (&w)[NTW][16]) {
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    uint32_t k = kb + t;
-    if constexpr (CLAMP) k = k < D0 ? k : D0 - 1;
-    const uint32_t off = k * D1 + col[0];
-    if constexpr (PAIR) {
-      const uint2 v = *reinterpret_cast<const uint2*>(dbp + off);
-      w[0][t] = v.x;
-      w[1][t] = v.y;
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) w[nt][t] = dbp[off + (col[nt] - col[0])];
-    }
-  }
-}
+#ifndef PIRSCAN_NT_STORE
+#define PIRSCAN_NT_STORE 1
+#endif
 
-// One wavefront = one point and NTW column tiles of 16; MT row tiles of 16.
-// PAIR: tile 0 takes the even and tile 1 the odd columns of a 32-column
-// block (D1 even), so a lane's two columns are one 64-bit word pair.
-template <int MT, int NTW, bool PAIR>
-__global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, MfmaEpilogue ep,
-                                                               const v4i* __restrict__ limbs,
-                                                               uint32_t* __restrict__ out_t,
-                                                               uint32_t m_base, uint32_t nblk,
-                                                               uint64_t items, uint32_t S) {
-  static_assert(!PAIR || NTW == 2, "paired columns need two tiles");
-  const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t li = lane % 16, lg = lane / 16;
-  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
-  const uint64_t item = (uint64_t)wg * (kThreads / 64) + wave;
-  if (item >= items) return;  // no barriers in this kernel
-  const uint64_t p = item / nblk;
-  const uint32_t n0 = (uint32_t)(item % nblk) * NTW * 16;
-  const uint32_t limb = (uint32_t)(p / a.N);
-  const uint32_t q = a.lc.q[limb], half = q / 2, bias_hi = 0x80808080u - q;
-  const uint32_t D0 = a.D0, D1 = a.D1;
-
-  // the column of this lane in tile nt, clamped (results past D1 are not stored)
-  uint32_t col[NTW], cout[NTW];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const uint32_t c = PAIR ? n0 + 2 * li + nt : n0 + nt * 16 + li;
-    cout[nt] = c;
-    if constexpr (PAIR) col[nt] = (n0 + 2 * li + 1) < D1 ? c : D1 - 2 + nt;  // D1 is even here
-    else col[nt] = c < D1 ? c : D1 - 1;
-  }
-  const uint32_t* dbp = a.dbt + p * (uint64_t)D0 * D1;  // D0*D1 < 2^31 words on this path
-
-  v4i acc[7][MT][NTW];
-#pragma unroll
-  for (int d = 0; d < 7; ++d)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) acc[d][mt][nt] = v4i{0, 0, 0, 0};
-
-  const v4i* lp = limbs + (p * S) * MT * 4 * 64 + lane;
-  for (uint32_t s = 0; s < S; ++s) {
-    v4i af[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) af[mt][j] = lp[(((uint64_t)s * MT + mt) * 4 + j) * 64];
-    uint32_t w[NTW][16];
-    const uint32_t kb = s * 64 + lg * 16;
-    if ((s + 1) * 64 <= D0) load_b_step<NTW, PAIR, false>(dbp, col, kb, D0, D1, w);
-    else load_b_step<NTW, PAIR, true>(dbp, col, kb, D0, D1, w);
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) w[nt][t] = centred_digits(w[nt][t], half, 0x80808080u, bias_hi);
-      v4i bf[4];
-      limb_fragments(w[nt], bf);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i + j][mt][nt] =
-                __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt][i], bf[j], acc[i + j][mt][nt], 0, 0, 0);
-    }
-  }
-
-  // Epilogue.  D element e of lane l is (row 4*(l/16) + e, column l%16 of the tile).
+// Epilogue of a wave: folds the seven diagonals of each accumulator element
+// into its residue and stores rows < m - m_base, columns < D1 of the wave's
+// tiles into out_t [P][m][D1].  D element e of lane (li, lg) is row
+// 4*lg + e, column li of the 16 x 16 tile.
+template <int MT, int NTW>
+__device__ __forceinline__ void store_outputs(const RowselLaunch& a, const MfmaEpilogue& ep,
+                                              const v4i (&acc)[7][MT][NTW], uint32_t* __restrict__ out_t,
+                                              uint64_t p, uint32_t g, uint32_t limb, uint32_t m_base, uint32_t lg,
+                                              uint32_t li) {
   const uint64_t c32 = a.lc.c[limb], mu = a.lc.mu[limb];
+  const uint32_t q = a.lc.q[limb];
   const uint32_t mrows = a.m - m_base;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -283,84 +211,319 @@ __global__ __launch_bounds__(kThreads) void rowsel_mfma_kernel(RowselLaunch a, M
       const uint32_t row = mt * 16 + 4 * lg + e;
       if (row >= mrows) continue;
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const uint32_t c = cout[nt];
-        if (c >= D1) continue;
+      for (int b = 0; b < NTW; ++b) {
+        const uint32_t c = (g * NTW + b) * 16 + li;
+        if (c >= a.D1) continue;
         uint64_t x = ep.corr[limb];
 #pragma unroll
-        for (int d = 0; d < 7; ++d) {
+        for (int dd = 0; dd < 7; ++dd) {
           x = (x >> 32) * c32 + (uint32_t)x;  // <= (2^32-1)(c32+1) < 2^63
-          x += (uint64_t)((uint32_t)acc[d][mt][nt][e] + 0x80000000u) * ep.w[limb][d];
+          x += (uint64_t)((uint32_t)acc[dd][mt][b][e] + 0x80000000u) * ep.w[limb][dd];
         }
         uint64_t r = x - __umul64hi(x, mu) * q;
         if (r >= q) r -= q;
-        out_t[((uint64_t)p * a.m + m_base + row) * D1 + c] = (uint32_t)r;
+        uint32_t* dst = out_t + ((uint64_t)p * a.m + m_base + row) * a.D1 + c;
+        if (PIRSCAN_NT_STORE) __builtin_nontemporal_store((uint32_t)r, dst);
+        else *dst = (uint32_t)r;
       }
     }
   }
 }
 
-uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+// s_waitcnt immediate: vmcnt = n (< 64), expcnt and lgkmcnt left unconstrained.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-struct MfmaWs {
-  uint64_t ct_t, limbs, out_t, total;  // byte offsets / size
+#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(x))
+
+// Workgroup = 4 wavefronts on one point p; wave w scans column tiles
+// (4g' + w) * NTW .. + NTW-1 (g' = the workgroup's quad of tile groups) over
+// every 64-k step, for MT row tiles of 16 (rows m_base ..).  Per step a wave
+// consumes NTW x 4 KiB of packed DB from HBM (register double buffer, one
+// step ahead) and MT x 4 KiB of A fragments from the shared LDS ring, and
+// issues 16 * MT * NTW MFMAs.  Waves past the last tile group run the same
+// loads, barriers and MFMAs on clamped tiles and store nothing.
+template <int MT, int NTW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2 : 3)))
+void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict__ limbs,
+                          const v4i* __restrict__ dbp, uint32_t* __restrict__ out_t, uint32_t m_base,
+                          uint32_t S, uint32_t T, uint32_t ngroups, uint32_t gq) {
+  constexpr int kAFrags = MT * 4;  // A fragments per step (row tile x limb)
+  __shared__ v4i aring[kRing][kAFrags * 64];
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t li = lane % 16, lg = lane / 16;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);  // grid = P * gq exactly
+  const uint64_t p = wg / gq;
+  const uint32_t g = (wg % gq) * 4 + wave;
+  const bool live = g < ngroups;
+  const uint32_t limb = (uint32_t)(p / a.N);
+
+  // this wave's column tiles (clamped for dead waves and the last group)
+  const v4i* bcol[NTW];
+#pragma unroll
+  for (int b = 0; b < NTW; ++b) {
+    const uint32_t t = g * NTW + b < T ? g * NTW + b : T - 1;
+    bcol[b] = dbp + ((p * T + t) * S) * kFrag + lane;
+  }
+  const v4i* ap = limbs + (p * S) * (uint64_t)(MT * kFrag) + lane;
+
+  v4i acc[7][MT][NTW];
+#pragma unroll
+  for (int dd = 0; dd < 7; ++dd)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int b = 0; b < NTW; ++b) acc[dd][mt][b] = v4i{0, 0, 0, 0};
+
+  v4i bb[2][NTW][4];
+  auto load_b = [&](int slot, uint32_t s) {
+    const uint32_t ss = s < S ? s : S - 1;  // past the end: a harmless reload of the last step
+#pragma unroll
+    for (int b = 0; b < NTW; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[slot][b][j] = __builtin_nontemporal_load(bcol[b] + ss * kFrag + j * 64);
+  };
+  // step s's A fragments -> ring slot s % kRing; wave w moves fragments w, w+4
+  auto issue_a = [&](uint32_t s) {
+    const uint32_t ss = s < S ? s : S - 1;
+    v4i* slot = aring[s % kRing];
+#pragma unroll
+    for (int h = 0; h < MT; ++h) {
+      const uint32_t f = wave + 4 * h;
+      __builtin_amdgcn_global_load_lds((const void*)(ap + (ss * kAFrags + f) * 64), LDS_PTR(slot + f * 64), 16,
+                                       0, 0);
+    }
+  };
+  // One step.  Issue order per step: B(s+1), then A(s+2); so at the wait of
+  // step s only A(s+1)'s MT loads may still be in flight, and B(s), A(s) have
+  // landed (A(s) was issued two steps back).  The barrier makes every wave's
+  // share of A(s) visible and tells each wave that all others have finished
+  // reading slot (s-1) % kRing, which A(s+2) then overwrites.  Scheduling
+  // barriers keep the order: ring reads, next loads, then the MFMAs (which
+  // would otherwise pull the next step's loads behind them).
+  auto step = [&](auto slot_tag, uint32_t s) {
+    constexpr int slot = decltype(slot_tag)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(MT));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const v4i* as = aring[s % kRing] + lane;
+    v4i af[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af[mt][j] = as[(mt * 4 + j) * 64];
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(slot ^ 1, s + 1);
+    issue_a(s + kRing - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NTW; ++b)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i + j][mt][b] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt][i], bb[slot][b][j], acc[i + j][mt][b], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  load_b(0, 0);
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r) issue_a(r);
+  uint32_t s = 0;
+  for (; s + 1 < S; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+  }
+  if (s < S) step(std::integral_constant<int, 0>{}, s);
+  __builtin_amdgcn_s_waitcnt(0);  // no ring load may outlive the workgroup's LDS
+
+  if (!live) return;
+  store_outputs<MT, NTW>(a, ep, acc, out_t, p, g, limb, m_base, lg, li);
+}
+
+// Small batches (one pass of at most 16 rows): no LDS ring and no barriers.
+// Each wave (point p, column tiles g*NTW .. g*NTW+NTW-1) loads its own A
+// fragments one step ahead with the DB fragments.  The A side is packed
+// compactly, lanes_per_group = mrows (only the live rows of each k-group), so
+// it costs the bytes of ct itself; lanes of rows past mrows read their group's
+// row-0 lane instead (same line, no branch).  Their output rows are copies of
+// row 0's and are never stored (MFMA rows are independent).
+template <int NTW>
+__global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLaunch a, MfmaEpilogue ep,
+                                                                        const v4i* __restrict__ limbs,
+                                                                        const v4i* __restrict__ dbp,
+                                                                        uint32_t* __restrict__ out_t,
+                                                                        uint32_t m_base, uint32_t S, uint32_t T,
+                                                                        uint32_t ngroups, uint64_t items) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t li = lane % 16, lg = lane / 16;
+  const uint64_t item = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
+  if (item >= items) return;  // no barriers in this kernel
+  const uint64_t p = item / ngroups;
+  const uint32_t g = (uint32_t)(item % ngroups);
+  const uint32_t limb = (uint32_t)(p / a.N);
+  const uint32_t mrows = a.m - m_base;  // 1..16: the compact A's lanes per k-group
+  const uint32_t astep = 16 * mrows;    // A fragments of one step: 4 limbs x 4 groups x mrows
+
+  const v4i* bcol[NTW];
+#pragma unroll
+  for (int b = 0; b < NTW; ++b) {
+    const uint32_t t = g * NTW + b < T ? g * NTW + b : T - 1;
+    bcol[b] = dbp + ((p * T + t) * S) * kFrag + lane;
+  }
+  const v4i* ap = limbs + p * S * astep + lg * mrows + (li < mrows ? li : 0);
+
+  v4i acc[7][1][NTW];
+#pragma unroll
+  for (int dd = 0; dd < 7; ++dd)
+#pragma unroll
+    for (int b = 0; b < NTW; ++b) acc[dd][0][b] = v4i{0, 0, 0, 0};
+  v4i aa[2][4], bb[2][NTW][4];
+  auto load = [&](int slot, uint32_t s) {
+    const uint32_t ss = s < S ? s : S - 1;  // past the end: a harmless reload of the last step
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aa[slot][j] = ap[ss * astep + j * 4 * mrows];
+#pragma unroll
+    for (int b = 0; b < NTW; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[slot][b][j] = __builtin_nontemporal_load(bcol[b] + ss * kFrag + j * 64);
+  };
+  auto step = [&](auto slot_tag, uint32_t s) {
+    constexpr int slot = decltype(slot_tag)::value;
+    load(slot ^ 1, s + 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next step's loads ahead of this step's MFMAs
+#pragma unroll
+    for (int b = 0; b < NTW; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i + j][0][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[slot][i], bb[slot][b][j], acc[i + j][0][b], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  load(0, 0);
+  uint32_t s = 0;
+  for (; s + 1 < S; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+  }
+  if (s < S) step(std::integral_constant<int, 0>{}, s);
+  store_outputs<1, NTW>(a, ep, acc, out_t, p, g, limb, m_base, lg, li);
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+uint32_t steps_of(uint32_t D0) { return (D0 + 63) / 64; }
+uint32_t tiles_of(uint32_t D1) { return (D1 + 15) / 16; }
+
+struct PackedWs {
+  uint64_t limbs, out_t, total;  // byte offsets / size
 };
 
-MfmaWs mfma_workspace(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1) {
-  const uint64_t S = (D0 + 63) / 64;
-  const uint32_t mt_max = m >= 32 ? 2 : (m + 15) / 16;
-  MfmaWs w{};
-  w.ct_t = 0;
-  w.limbs = align256(4ull * P * m * D0);
-  w.out_t = w.limbs + align256(P * S * mt_max * 4 * 64 * 16);
+// A fragments of the largest pass: the direct kernel's compact m x 4 limbs x
+// 4 groups per step (m <= 16), else two whole 16-row tiles.
+PackedWs packed_workspace(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1) {
+  const uint64_t a_step = m <= kDirectRows ? 16ull * m : 2ull * kFrag;  // v4i per point and step
+  PackedWs w{};
+  w.limbs = 0;
+  w.out_t = align256((uint64_t)P * steps_of(D0) * a_step * 16);
   w.total = w.out_t + align256(4ull * P * m * D1);
   return w;
 }
 
 template <int MT, int NTW>
-hipError_t launch_mfma_pass(const RowselLaunch& a, const MfmaEpilogue& ep, const v4i* limbs,
-                            uint32_t* out_t, uint32_t m_base, uint32_t S, hipStream_t stream) {
-  const uint32_t nblk = (a.D1 + NTW * 16 - 1) / (NTW * 16);
-  const uint64_t items = a.P * nblk;
-  const uint64_t grid = (items + 3) / 4;
+hipError_t launch_scan(const RowselLaunch& a, const MfmaEpilogue& ep, const v4i* limbs, const v4i* dbp,
+                       uint32_t* out_t, uint32_t m_base, hipStream_t stream) {
+  const uint32_t S = steps_of(a.D0), T = tiles_of(a.D1);
+  const uint32_t ngroups = (T + NTW - 1) / NTW, gq = (ngroups + 3) / 4;
+  const uint64_t grid = a.P * gq;
   if (grid == 0 || grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  // adjacent column pairs need an even row length (8-byte aligned pairs)
-  if (a.D1 % 2 == 0)
-    hipLaunchKernelGGL((rowsel_mfma_kernel<MT, NTW, true>), dim3((uint32_t)grid), dim3(kThreads), 0, stream,
-                       a, ep, limbs, out_t, m_base, nblk, items, S);
-  else
-    hipLaunchKernelGGL((rowsel_mfma_kernel<MT, NTW, false>), dim3((uint32_t)grid), dim3(kThreads), 0,
-                       stream, a, ep, limbs, out_t, m_base, nblk, items, S);
+  hipLaunchKernelGGL((rowsel_packed_kernel<MT, NTW>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, a, ep,
+                     limbs, dbp, out_t, m_base, S, T, ngroups, gq);
   return hipGetLastError();
 }
 
-uint32_t grid_for(uint64_t items) {
-  uint64_t g = (items + kThreads - 1) / kThreads;
-  if (g > (1u << 20)) g = 1u << 20;
-  return (uint32_t)(g ? g : 1);
+template <int NTW>
+hipError_t launch_scan_direct(const RowselLaunch& a, const MfmaEpilogue& ep, const v4i* limbs, const v4i* dbp,
+                              uint32_t* out_t, uint32_t m_base, hipStream_t stream) {
+  const uint32_t S = steps_of(a.D0), T = tiles_of(a.D1);
+  const uint32_t ngroups = (T + NTW - 1) / NTW;
+  const uint64_t items = a.P * ngroups, grid = (items + 3) / 4;
+  if (grid == 0 || grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((rowsel_packed_direct_kernel<NTW>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, a, ep,
+                     limbs, dbp, out_t, m_base, S, T, ngroups, items);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-bool rowsel_mfma_eligible(const RowselLaunch& a, uint32_t R) {
-  if (a.m < kRowselMfmaMinRows || a.D0 > 16384) return false;
-  if ((uint64_t)a.D0 * a.D1 >= (1ull << 31)) return false;  // 32-bit word offsets within a point
+bool rowsel_packed_ok(const uint32_t* q, uint32_t R, uint32_t D0) {
+#ifdef PIRSCAN_FORCE_VALU
+  return false;
+#endif
+  if (D0 > kPackedMaxD0) return false;
   for (uint32_t r = 0; r < R; ++r)
-    if (a.lc.q[r] >= (1u << 31)) return false;
+    if (q[r] >= (1u << 31)) return false;
   return true;
 }
 
-size_t rowsel_mfma_workspace_bytes(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1) {
-  return (size_t)mfma_workspace(P, m, D0, D1).total;
+uint64_t packed_layout_bytes(uint64_t P, uint32_t D0, uint32_t D1) {
+  return P * tiles_of(D1) * steps_of(D0) * (uint64_t)kFrag * 16;
 }
 
-hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace, hipStream_t stream) {
-  const MfmaWs ws = mfma_workspace(a.P, a.m, a.D0, a.D1);
+hipError_t launch_pack(const PackDesc& d, hipStream_t stream) {
+  auto a16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+  if (d.P % 4 == 0 && d.s_row % 4 == 0 && d.s_k % 4 == 0 && a16(d.src)) {
+    const uint64_t pblocks = (d.P + kPackPoints - 1) / kPackPoints;
+    const uint64_t total = pblocks * 4 * d.tiles * d.S;
+    const uint64_t grid = total < (1ull << 20) ? total : (1ull << 20);
+    hipLaunchKernelGGL(pack_limbs4_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, d, pblocks, total);
+  } else {
+    const uint64_t total = d.P * d.tiles * d.S * 64;
+    uint64_t grid = (total + kThreads - 1) / kThreads;
+    if (grid > (1u << 20)) grid = 1u << 20;
+    hipLaunchKernelGGL(pack_limbs_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, d, total);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_operand(const uint32_t* src, void* dst, uint64_t P, uint32_t N, const uint32_t* q,
+                               uint32_t R, uint32_t rows, uint32_t K, uint64_t s_row, uint64_t s_k,
+                               hipStream_t stream) {
+  PackDesc d{};
+  d.src = src;
+  d.dst = dst;
+  d.P = P;
+  d.N = N;
+  d.rows = rows;
+  d.row_base = 0;
+  d.K = K;
+  d.s_row = s_row;
+  d.s_k = s_k;
+  d.tiles = tiles_of(rows);
+  d.S = steps_of(K);
+  d.lpg = 16;
+  d.d_s = kFrag;
+  d.d_t = (uint64_t)d.S * kFrag;
+  d.d_p = (uint64_t)d.tiles * d.d_t;
+  for (uint32_t r = 0; r < R; ++r) d.q[r] = q[r];
+  return launch_pack(d, stream);
+}
+
+size_t rowsel_packed_workspace_bytes(uint64_t P, uint32_t m, uint32_t D0, uint32_t D1) {
+  return (size_t)packed_workspace(P, m, D0, D1).total;
+}
+
+hipError_t launch_rowsel_packed(const RowselLaunch& a, uint32_t R, void* workspace, hipStream_t stream) {
+  const PackedWs ws = packed_workspace(a.P, a.m, a.D0, a.D1);
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  uint32_t* ct_t = reinterpret_cast<uint32_t*>(base + ws.ct_t);
   v4i* limbs = reinterpret_cast<v4i*>(base + ws.limbs);
   uint32_t* out_t = reinterpret_cast<uint32_t*>(base + ws.out_t);
-  const uint32_t S = (a.D0 + 63) / 64;
+  const v4i* dbp = reinterpret_cast<const v4i*>(a.dbt);
+  const uint32_t S = steps_of(a.D0);
 
   MfmaEpilogue ep{};
   for (uint32_t r = 0; r < R; ++r) {
@@ -374,50 +537,36 @@ hipError_t launch_rowsel_mfma(const RowselLaunch& a, uint32_t R, void* workspace
     ep.corr[r] = (uint32_t)((q - off) % q);
   }
 
-  // ct -> A fragments in one pass where the 16-byte point runs are aligned
-  const bool fused = a.P % 4 == 0 && a.ct_sm % 4 == 0 && a.ct_sk % 4 == 0 &&
-                     reinterpret_cast<uintptr_t>(a.ct) % 16 == 0;
   hipError_t e = hipSuccess;
-  if (fused) {
-    const uint64_t pblocks = (a.P + kPrepPoints - 1) / kPrepPoints;
-    for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
-      const uint32_t MT = a.m - m_base > 16 ? 2 : 1;
-      const uint64_t grid = pblocks * 4 * MT * S;
-      if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(rowsel_prep_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a, limbs,
-                         m_base, MT, S, (uint32_t)pblocks);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      timer_mark_start(stream);  // first pass only
-      if (MT == 2) e = launch_mfma_pass<2, 2>(a, ep, limbs, out_t, m_base, S, stream);
-      else e = launch_mfma_pass<1, 2>(a, ep, limbs, out_t, m_base, S, stream);
-      if (e != hipSuccess) return e;
-    }
-    timer_mark_stop(stream);
-    return launch_out_relayout(a, out_t, stream);
-  }
-
-  // otherwise: ct(mi, k, p) -> ct_t [P][m][D0], then the limb split
-  TransposeDesc tc{};
-  tc.src = a.ct;
-  tc.dst = ct_t;
-  tc.batch = a.m;
-  tc.rows = a.D0;
-  tc.cols = a.P;
-  tc.s_batch = a.ct_sm;
-  tc.s_row = a.ct_sk;
-  tc.d_batch = a.D0;
-  tc.d_row = (uint64_t)a.m * a.D0;
-  e = launch_transpose(tc, stream);
-  if (e != hipSuccess) return e;
   for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
-    const uint32_t rows = a.m - m_base;
-    const uint32_t MT = rows > 16 ? 2 : 1;
-    hipLaunchKernelGGL(rowsel_limbs_kernel, dim3(grid_for(a.P * S * MT * 64)), dim3(kThreads), 0, stream,
-                       ct_t, limbs, a.P, a.m, a.D0, m_base, MT, S, a.N, a.lc);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint32_t rows = a.m - m_base < 32 ? a.m - m_base : 32;
+    const bool direct = rows <= kDirectRows;
+    // ct rows m_base .. m_base + rows -> A fragments [p][s][row tile][limb][group][lane]:
+    // whole 16-lane groups for the ring kernel, only the live rows for the direct one
+    PackDesc d{};
+    d.src = a.ct;
+    d.dst = limbs;
+    d.P = a.P;
+    d.N = a.N;
+    d.rows = a.m;
+    d.row_base = m_base;
+    d.K = a.D0;
+    d.s_row = a.ct_sm;
+    d.s_k = a.ct_sk;
+    d.tiles = direct ? 1 : 2;
+    d.lpg = direct ? rows : 16;
+    d.S = S;
+    d.d_t = 16ull * d.lpg;
+    d.d_s = d.tiles * d.d_t;
+    d.d_p = (uint64_t)S * d.d_s;
+    for (uint32_t r = 0; r < R; ++r) d.q[r] = a.lc.q[r];
+    if ((e = launch_pack(d, stream)) != hipSuccess) return e;
     timer_mark_start(stream);  // first pass only
-    if (MT == 2) e = launch_mfma_pass<2, 2>(a, ep, limbs, out_t, m_base, S, stream);
-    else e = launch_mfma_pass<1, 2>(a, ep, limbs, out_t, m_base, S, stream);
+    // one column tile per wave while the A stream is small next to the DB's
+    // (rows <= 4: at most a quarter), four beyond, which divides it by four
+    if (direct && rows <= 4) e = launch_scan_direct<1>(a, ep, limbs, dbp, out_t, m_base, stream);
+    else if (direct) e = launch_scan_direct<4>(a, ep, limbs, dbp, out_t, m_base, stream);
+    else e = launch_scan<2, 2>(a, ep, limbs, dbp, out_t, m_base, stream);
     if (e != hipSuccess) return e;
   }
   timer_mark_stop(stream);

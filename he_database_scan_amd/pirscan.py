@@ -99,11 +99,25 @@ class PirscanError(RuntimeError):
 _lib = None
 
 
+def _init_torch_device():
+    """torch and libpirscan each carry a HIP runtime.  The library's must start
+    after torch's has opened the device: loaded first, it later finds no
+    device (hipErrorNoDevice on its first call).  So torch's comes up first
+    wherever a GPU is present."""
+    try:
+        import torch
+    except ImportError:
+        return
+    if torch.cuda.is_available():
+        torch.cuda.init()
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libpirscan is not built ({LIB_PATH}); run __graft_entry__.build()")
+        _init_torch_device()
         L = ctypes.CDLL(LIB_PATH)
         vp, u32, u64, sz = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t
         shp = ctypes.POINTER(RowselShape)
@@ -185,6 +199,15 @@ def _dev(t, name: str, elem: int, numel: int):
                          f"{t.numel()} of {t.element_size()}")
 
 
+def _dev_bytes(t, name: str, nbytes: int):
+    """A contiguous device buffer of any dtype holding at least nbytes."""
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: expected a contiguous buffer of at least {nbytes} bytes, got "
+                         f"{t.numel() * t.element_size()}")
+
+
 # ---- entry points -----------------------------------------------------------
 
 def version() -> int:
@@ -200,10 +223,10 @@ def layout_db_bytes(shape: RowselShape) -> int:
 
 
 def layout_db(shape: RowselShape, db_pmajor, db_tiled, stream=None) -> None:
-    """db_pmajor [D0][D1][P] (uint32 bits) -> db_tiled (same word count)."""
-    n = shape.D0 * shape.D1 * shape.P
-    _dev(db_pmajor, "db_pmajor", 4, n)
-    _dev(db_tiled, "db_tiled", 4, n)
+    """db_pmajor [D0][D1][P] (uint32 bits) -> db_tiled, a device buffer of at
+    least ``layout_db_bytes(shape)`` bytes (any dtype)."""
+    _dev(db_pmajor, "db_pmajor", 4, shape.D0 * shape.D1 * shape.P)
+    _dev_bytes(db_tiled, "db_tiled", layout_db_bytes(shape))
     _check("pirscan_layout_db",
            _load().pirscan_layout_db(ctypes.byref(shape), _ptr(db_pmajor), _ptr(db_tiled), _stream(stream)))
 
@@ -220,7 +243,7 @@ def rowsel_modgemm(shape: RowselShape, m: int, ct, db_tiled, out, workspace=None
     """
     P = shape.P
     _dev(ct, "ct", 4, m * shape.D0 * P)
-    _dev(db_tiled, "db_tiled", 4, shape.D0 * shape.D1 * P)
+    _dev_bytes(db_tiled, "db_tiled", layout_db_bytes(shape))
     _dev(out, "out", 4, m * shape.D1 * P)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pirscan_rowsel_modgemm",
@@ -233,10 +256,10 @@ def exppack_layout_h_bytes(shape: ExppackShape) -> int:
 
 
 def exppack_layout_h(shape: ExppackShape, h_pmajor, h_tiled, stream=None) -> None:
-    """h_pmajor [Dr][n][P] (uint32 bits) -> h_tiled (same word count)."""
-    n = shape.Dr * shape.n * shape.P
-    _dev(h_pmajor, "h_pmajor", 4, n)
-    _dev(h_tiled, "h_tiled", 4, n)
+    """h_pmajor [Dr][n][P] (uint32 bits) -> h_tiled, a device buffer of at
+    least ``exppack_layout_h_bytes(shape)`` bytes (any dtype)."""
+    _dev(h_pmajor, "h_pmajor", 4, shape.Dr * shape.n * shape.P)
+    _dev_bytes(h_tiled, "h_tiled", exppack_layout_h_bytes(shape))
     _check("pirscan_exppack_layout_h",
            _load().pirscan_exppack_layout_h(ctypes.byref(shape), _ptr(h_pmajor), _ptr(h_tiled),
                                             _stream(stream)))
@@ -255,7 +278,7 @@ def exppack_modgemm(shape: ExppackShape, B: int, C, h_tiled, G, out, workspace=N
     """
     P = shape.P
     _dev(C, "C", 4, shape.n * 2 * B * P)
-    _dev(h_tiled, "h_tiled", 4, shape.Dr * shape.n * P)
+    _dev_bytes(h_tiled, "h_tiled", exppack_layout_h_bytes(shape))
     if G is not None:
         _dev(G, "G", 4, shape.Dr * B * P)
     _dev(out, "out", 4, shape.Dr * 2 * B * P)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PIRSCAN_VERSION 10200 /* 1.2.0 */
+#define PIRSCAN_VERSION 10300 /* 1.3.0 */
 #define PIRSCAN_MAX_R 8
 
 enum {
@@ -75,8 +75,12 @@ typedef struct {
   uint32_t D1;                 /* n extent */
 } pirscan_rowsel_shape;
 
-/* Bytes of the tiled RowSel database produced by pirscan_layout_db:
- * exactly 4 * P * D0 * D1 (no padding).  0 if the shape is invalid. */
+/* Bytes of the tiled RowSel database produced by pirscan_layout_db, or 0 if
+ * the shape is invalid.  When every q[r] < 2^31 and D0 <= 16384 the database
+ * is stored for the int8 matrix-core scan: per point, ceil(D1/16) column
+ * tiles x ceil(D0/64) k-steps x 4 KiB (exactly 4 * P * D0 * D1 when 16 | D1
+ * and 64 | D0).  Otherwise it is stored word for word for the 64-bit VALU
+ * scan: 4 * P * D0 * D1. */
 size_t pirscan_layout_db_bytes(const pirscan_rowsel_shape* s);
 
 /*
@@ -86,20 +90,26 @@ size_t pirscan_layout_db_bytes(const pirscan_rowsel_shape* s);
  *   db_pmajor : [D0][D1][P] uint32, p-major (the HE-library/NTT layout in which
  *               each polynomial's P points are contiguous; GPIR layout
  *               paragraph).  Entries must be < q[p / N].
- *   db_tiled  : pirscan_layout_db_bytes(s) bytes, written in the library's
- *               internal layout (opaque; consumed by pirscan_rowsel_modgemm).
- * Must not overlap.  Pure permutation of words; no arithmetic.
+ *   db_tiled  : pirscan_layout_db_bytes(s) bytes, 16-byte aligned, written in
+ *               the library's internal layout (opaque; consumed by
+ *               pirscan_rowsel_modgemm with the same shape).  For the matrix-
+ *               core scan every residue is centred (x - q when x > q/2) and
+ *               split into four signed 8-bit limbs (VIPIR section 4.1's INT8
+ *               decomposition), stored in the order of the scan's fragments.
+ * Must not overlap.  EINVAL for a misaligned db_tiled on the matrix-core
+ * layout.
  */
 int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor,
                       uint32_t* db_tiled, void* stream);
 
 /*
- * Workspace bytes pirscan_rowsel_modgemm needs for (shape, m): room for the
- * per-point staging of the output (4 * P * m * D1 bytes, rounded up to 256),
- * and, when the batch runs on int8 MFMA (m >= 16, every modulus < 2^31,
- * D0 <= 16384, D0 * D1 < 2^31; GPIR: batching makes RowSel a dense
- * contraction), for the
- * per-query relayout of ct as well.  0 only on an invalid shape or m == 0.
+ * Workspace bytes pirscan_rowsel_modgemm needs for (shape, m), 0 only on an
+ * invalid shape or m == 0: the per-point staging of the output (4 * P * m *
+ * D1 bytes) and, on the matrix-core scan (every q < 2^31, D0 <= 16384; GPIR:
+ * batching makes RowSel a dense contraction, and at batch 1 the scan streams
+ * the same bytes), the per-query limb split of ct: 16 * m bytes per point and
+ * 64-k step for m <= 16, else 8 KiB (passes of 32 rows).  Each part is
+ * rounded up to 256 bytes.
  */
 size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m);
 
@@ -135,8 +145,9 @@ typedef struct {
   uint32_t n;                  /* LWE dimension: columns of H, rows of C */
 } pirscan_exppack_shape;
 
-/* Bytes of the tiled hint produced by pirscan_exppack_layout_h: exactly
- * 4 * P * Dr * n.  0 if the shape is invalid. */
+/* Bytes of the tiled hint produced by pirscan_exppack_layout_h, or 0 if the
+ * shape is invalid: as pirscan_layout_db_bytes with D0 = n and D1 = Dr
+ * (exactly 4 * P * Dr * n = 15 GiB at section 3.6's sizes). */
 size_t pirscan_exppack_layout_h_bytes(const pirscan_exppack_shape* s);
 
 /*
@@ -145,19 +156,19 @@ size_t pirscan_exppack_layout_h_bytes(const pirscan_exppack_shape* s);
  * packing streams; section 4.2 transposes between the polynomial-major NTT
  * layout and the GEMM layout).
  *   h_pmajor : [Dr][n][P] uint32, p-major, entries < q[p / N].
- *   h_tiled  : pirscan_exppack_layout_h_bytes(s) bytes, opaque layout consumed
- *              by pirscan_exppack_modgemm.
- * Must not overlap.  Pure permutation of words.
+ *   h_tiled  : pirscan_exppack_layout_h_bytes(s) bytes, 16-byte aligned,
+ *              opaque layout consumed by pirscan_exppack_modgemm (the limb
+ *              split of pirscan_layout_db when every q < 2^31 and n <= 16384,
+ *              else a word transpose).
+ * Must not overlap.
  */
 int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_pmajor,
                              uint32_t* h_tiled, void* stream);
 
 /*
- * Workspace bytes pirscan_exppack_modgemm needs for (shape, B): room for the
- * per-point staging of the output (4 * P * 2B * Dr bytes, rounded up to 256)
- * and, when the batch runs on int8 MFMA (2B >= 16, every modulus < 2^31,
- * n <= 16384, n * Dr < 2^31), for the per-query relayout of C.  0 only on an invalid shape
- * or B == 0.
+ * Workspace bytes pirscan_exppack_modgemm needs for (shape, B): as
+ * pirscan_rowsel_workspace_bytes with m = 2B, D0 = n and D1 = Dr.  0 only on
+ * an invalid shape or B == 0.
  */
 size_t pirscan_exppack_workspace_bytes(const pirscan_exppack_shape* s, uint32_t B);
 

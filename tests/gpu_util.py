@@ -42,6 +42,13 @@ def empty_u32(shape):
     return torch.empty(shape, dtype=torch.int32, device=torch_dev())
 
 
+def empty_bytes(nbytes):
+    """A device buffer of nbytes (the relaid DB / hint operands)."""
+    import torch
+
+    return torch.empty(nbytes, dtype=torch.uint8, device=torch_dev())
+
+
 def release():
     import torch
 

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert pirscan.version() == 10200
+    assert pirscan.version() == 10300
     assert pirscan.strerror(0) == "ok"
     assert "invalid" in pirscan.strerror(-1)
     assert "gfx950" in pirscan.strerror(-3)
@@ -51,7 +51,13 @@ Q3 = [536813569, 536690689, 536641537]
 
 def test_layout_bytes_and_invalid_shapes():
     s = pirscan.RowselShape.make(4096, Q3, 1024, 1024)
-    assert pirscan.layout_db_bytes(s) == 51539607552  # 48 GiB
+    assert pirscan.layout_db_bytes(s) == 51539607552  # 48 GiB: the packed limbs are exactly the words
+    # packed (every q < 2^31, D0 <= 16384): per point ceil(D1/16) x ceil(D0/64) x 4 KiB fragments
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(16, Q3, 65, 17)) == 48 * 2 * 2 * 4096
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(4, [7], 1, 1)) == 4 * 4096
+    # word layout for the VALU scan: a modulus >= 2^31, or D0 > 16384
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(16, [2147483659], 65, 17)) == 4 * 16 * 65 * 17
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(4, Q3, 16385, 3)) == 4 * 12 * 16385 * 3
     bad = [pirscan.RowselShape.make(0, Q3, 4, 4), pirscan.RowselShape.make(4, Q3, 0, 4),
            pirscan.RowselShape.make(4, Q3, 4, 0), pirscan.RowselShape.make(4, [1], 4, 4),
            pirscan.RowselShape.make(4, [0, 7], 4, 4)]
@@ -84,15 +90,18 @@ def test_page_size_identities():
 def test_rowsel_workspace_sizes():
     s = pirscan.RowselShape.make(4096, Q3, 1024, 1024)
     P = 12288
-    assert pirscan.rowsel_workspace_bytes(s, 2) == 4 * P * 2 * 1024    # VALU: output staging only
-    assert pirscan.rowsel_workspace_bytes(s, 15) == 4 * P * 15 * 1024
-    ct = out = 4 * P * 32 * 1024
-    limbs = P * 16 * 2 * 4 * 64 * 16                            # 16 k-steps, 2 row tiles, 4 limbs
-    assert pirscan.rowsel_workspace_bytes(s, 32) == ct + limbs + out
+    # MFMA path: A fragments of the largest pass + output staging.  Up to 16 rows
+    # the fragments hold only the live rows (m x 4 limbs x 4 k-groups x 16 bytes
+    # per 64-k step: the bytes of ct); beyond, two whole 16-row tiles (8 KiB per step)
+    limbs2 = P * 16 * 2 * 4096
+    assert pirscan.rowsel_workspace_bytes(s, 2) == P * 16 * 256 * 2 + 4 * P * 2 * 1024
+    assert pirscan.rowsel_workspace_bytes(s, 15) == P * 16 * 256 * 15 + 4 * P * 15 * 1024
+    assert pirscan.rowsel_workspace_bytes(s, 32) == limbs2 + 4 * P * 32 * 1024
+    assert pirscan.rowsel_workspace_bytes(s, 40) == limbs2 + 4 * P * 40 * 1024   # passes of 32 rows
     big_q = pirscan.RowselShape.make(16, [2147483659], 64, 64)  # a modulus >= 2^31: VALU path
     assert pirscan.rowsel_workspace_bytes(big_q, 32) == 4 * 16 * 32 * 64
     assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(16, Q3, 20000, 64), 32) == 4 * 48 * 32 * 64
-    assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(1, [7], 1, 1), 1) == 256   # rounded up
+    assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(1, [7], 1, 1), 1) == 256 + 256
     assert pirscan.rowsel_workspace_bytes(s, 0) == 0
 
 
@@ -151,11 +160,13 @@ def test_exppack_sizes():
     s = pirscan.ExppackShape.make(4096, Q3, 256, 1280)
     assert pirscan.exppack_layout_h_bytes(s) == 15 * (1 << 30)
     P = 12288
-    assert pirscan.exppack_workspace_bytes(s, 1) == 4 * P * 2 * 256     # m = 2: VALU, output staging
-    assert pirscan.exppack_workspace_bytes(s, 7) == 4 * P * 14 * 256    # m = 14
-    ct, out = 4 * P * 32 * 1280, 4 * P * 32 * 256
-    limbs = P * 20 * 2 * 4 * 64 * 16                              # 20 k-steps of 64, 2 row tiles
-    assert pirscan.exppack_workspace_bytes(s, 16) == ct + limbs + out
+    limbs2 = P * 20 * 2 * 4096                                    # 20 k-steps of 64, 2 row tiles
+    assert pirscan.exppack_workspace_bytes(s, 1) == P * 20 * 256 * 2 + 4 * P * 2 * 256     # m = 2
+    assert pirscan.exppack_workspace_bytes(s, 7) == P * 20 * 256 * 14 + 4 * P * 14 * 256   # m = 14
+    assert pirscan.exppack_workspace_bytes(s, 16) == limbs2 + 4 * P * 32 * 256
+    big = pirscan.ExppackShape.make(4096, [4294967291], 256, 1280)              # VALU: output staging
+    assert pirscan.exppack_workspace_bytes(big, 1) == 4 * 4096 * 2 * 256
+    assert pirscan.exppack_layout_h_bytes(big) == 4 * 4096 * 256 * 1280
     assert pirscan.exppack_workspace_bytes(s, 0) == 0
     for bad in (pirscan.ExppackShape.make(0, Q3, 4, 4), pirscan.ExppackShape.make(4, Q3, 0, 4),
                 pirscan.ExppackShape.make(4, Q3, 4, 0), pirscan.ExppackShape.make(4, [1], 4, 4)):

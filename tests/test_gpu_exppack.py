@@ -11,7 +11,7 @@ import pytest
 import oracle
 import synth
 from he_database_scan_amd import pirscan
-from tests.gpu_util import MED_Q, TINY_Q, empty_u32, release, say, to_dev_u32, to_host_u32
+from tests.gpu_util import MED_Q, TINY_Q, empty_bytes, empty_u32, release, say, to_dev_u32, to_host_u32
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,7 @@ def run_gpu(H, C, G, N, q):
     Dr, n, P = H.shape
     B = C.shape[1] // 2
     shape = pirscan.ExppackShape.make(N, q, Dr, n)
-    d_ht = empty_u32(H.shape)
+    d_ht = empty_bytes(pirscan.exppack_layout_h_bytes(shape))
     pirscan.exppack_layout_h(shape, to_dev_u32(H), d_ht)
     d_out = empty_u32((Dr, 2 * B, P))
     pirscan.exppack_modgemm(shape, B, to_dev_u32(C), d_ht, None if G is None else to_dev_u32(G), d_out,
@@ -94,7 +94,7 @@ def test_one_hot_selects_hint_column(B):
     rng = np.random.default_rng(70 + B)
     H = rand_res(rng, (Dr, n, P), N, q)
     shape = pirscan.ExppackShape.make(N, q, Dr, n)
-    d_ht = empty_u32(H.shape)
+    d_ht = empty_bytes(pirscan.exppack_layout_h_bytes(shape))
     pirscan.exppack_layout_h(shape, to_dev_u32(H), d_ht)
     d_out = empty_u32((Dr, 2 * B, P))
     ws = workspace(shape, B)
@@ -134,7 +134,7 @@ def sampled_full_size(seed, B_list, points):
     say(f"exppack full size: synthesising {4 * P * Dr * n / 2**30:.1f} GiB hint")
     d_h = empty_u32((Dr, n, P))
     synth.fill_residues_(d_h, seed, synth.STREAM_EXPPACK_H, N, q)
-    d_ht = empty_u32((P, n, Dr))
+    d_ht = empty_bytes(pirscan.exppack_layout_h_bytes(shape))
     pirscan.exppack_layout_h(shape, d_h, d_ht)
     del d_h
     release()

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from he_database_scan_amd import pirscan
-from tests.gpu_util import MED_Q, empty_u32, say, to_dev_u32
+from tests.gpu_util import MED_Q, empty_bytes, empty_u32, say, to_dev_u32
 
 pytestmark = pytest.mark.gpu
 
@@ -17,7 +17,7 @@ def test_one_time_per_call_within_the_call():
     N, D0, D1 = 64, 256, 512
     P = N * len(MED_Q)
     shape = pirscan.RowselShape.make(N, MED_Q, D0, D1)
-    dbt = empty_u32((P, D0, D1))
+    dbt = empty_bytes(pirscan.layout_db_bytes(shape))
     pirscan.layout_db(shape, to_dev_u32(rng.integers(0, MED_Q[2], size=(D0, D1, P))), dbt)
     calls = []
     for m in (2, 32):

@@ -9,7 +9,7 @@ import pytest
 import oracle
 import synth
 from he_database_scan_amd import pirscan
-from tests.gpu_util import MED_Q, TINY_Q, empty_u32, release, say, to_dev_u32, to_host_u32
+from tests.gpu_util import MED_Q, TINY_Q, empty_bytes, empty_u32, release, say, to_dev_u32, to_host_u32
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,7 @@ def run_gpu(ct, db, N, q):
     D1 = db.shape[1]
     shape = pirscan.RowselShape.make(N, q, D0, D1)
     d_db = to_dev_u32(db)
-    d_dbt = empty_u32(db.shape)
+    d_dbt = empty_bytes(pirscan.layout_db_bytes(shape))
     pirscan.layout_db(shape, d_db, d_dbt)
     d_out = empty_u32((m, D1, P))
     pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out, workspace(shape, m))
@@ -52,7 +52,7 @@ def test_tiny_one_hot_rows_and_all_max():
     P = 2 * N
     db = synth.residue_array(1, synth.STREAM_ROWSEL_DB, (D0, D1, P), N, TINY_Q)
     shape = pirscan.RowselShape.make(N, TINY_Q, D0, D1)
-    d_dbt = empty_u32(db.shape)
+    d_dbt = empty_bytes(pirscan.layout_db_bytes(shape))
     pirscan.layout_db(shape, to_dev_u32(db), d_dbt)
     d_out = empty_u32((m, D1, P))
     for k in range(D0):
@@ -127,7 +127,7 @@ def sampled_full_size(seed, D0, D1, m, points, ct_stream=synth.STREAM_ROWSEL_CT)
     say(f"rowsel full size D0={D0} D1={D1} m={m}: synthesising {4 * P * D0 * D1 / 2**30:.1f} GiB")
     d_db = empty_u32((D0, D1, P))
     synth.fill_residues_(d_db, seed, synth.STREAM_ROWSEL_DB, N, q)
-    d_dbt = empty_u32((P, D0, D1))
+    d_dbt = empty_bytes(pirscan.layout_db_bytes(shape))
     pirscan.layout_db(shape, d_db, d_dbt)
     del d_db
     release()
@@ -202,3 +202,59 @@ def test_batched_path_point_counts(N, q, m, D0, D1):
     ct = rand_res(rng, (m, D0, P), N, q)
     db = rand_res(rng, (D0, D1, P), N, q)
     np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))
+
+
+def test_every_batch_size_on_one_layout():
+    """One relaid DB serves every m: 1..17 (one 16-row tile, then two), 31..33
+    (two tiles, then a second 32-row pass), on ragged D0 / D1 (partial k-step,
+    partial column tile, column-tile groups that leave waves of the last
+    workgroup without work)."""
+    import torch
+
+    N, q, D0, D1 = 4, MED_Q, 130, 300
+    P = N * len(q)
+    rng = np.random.default_rng(77)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    shape = pirscan.RowselShape.make(N, q, D0, D1)
+    d_dbt = empty_bytes(pirscan.layout_db_bytes(shape))
+    pirscan.layout_db(shape, to_dev_u32(db), d_dbt)
+    for m in list(range(1, 18)) + [31, 32, 33]:
+        say(f"rowsel one layout m={m}")
+        ct = rand_res(rng, (m, D0, P), N, q)
+        d_out = empty_u32((m, D1, P))
+        pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out, workspace(shape, m))
+        np.testing.assert_array_equal(to_host_u32(d_out), oracle.rowsel(ct, db, N, q))
+        del d_out
+    torch.cuda.synchronize()
+
+
+def signed_limb_value(digits):
+    return sum(int(d) << (8 * i) for i, d in enumerate(digits))
+
+
+@pytest.mark.parametrize("m", [2, 32])
+def test_limb_diagonals_at_the_largest_reduction(m):
+    """D0 = 16384, the largest k extent of the limb path: inputs whose centred
+    values have the largest digits a modulus below 2^31 allows (-128, -128,
+    -128, -63) and (127, 127, 127, 63) drive every int32 diagonal sum to its
+    extreme (4 pairs x D0 x 2^14 bounds it by 2^30).  D0 = 16385 takes the
+    64-bit VALU scan on a word-transposed layout."""
+    q = [2147483647, 2147483629]
+    N, D1 = 2, 16
+    P = N * len(q)
+    qv = np.asarray(q, dtype=np.int64)[np.arange(P) // N]
+    neg = signed_limb_value([-128, -128, -128, -63])
+    pos = signed_limb_value([127, 127, 127, 63])
+    assert -neg <= q[1] // 2 and pos <= q[1] // 2
+    xneg = (qv + neg).astype(np.uint32)
+    xpos = np.full(P, pos, dtype=np.uint32)
+    for D0 in (16384, 16385):
+        say(f"rowsel limb extremes m={m} D0={D0}")
+        for a, b in ((xneg, xneg), (xneg, xpos), (xpos, xpos)):
+            ct = np.broadcast_to(a, (m, D0, P)).copy()
+            db = np.broadcast_to(b, (D0, D1, P)).copy()
+            np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))
+        rng = np.random.default_rng(D0 + m)
+        ct = np.where(rng.integers(0, 2, size=(m, D0, P)) == 1, xneg, xpos).astype(np.uint32)
+        db = np.where(rng.integers(0, 2, size=(D0, D1, P)) == 1, xneg, xpos).astype(np.uint32)
+        np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))

@@ -23,7 +23,8 @@ HIPCC = "/opt/rocm/bin/hipcc"
 def test_every_kernel_has_a_terminated_body(src, tmp_path):
     out = tmp_path / "dev.s"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
-                    "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S", "-o", str(out), src],
+                    "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "--cuda-device-only",
+                    "-S", "-o", str(out), src],
                    check=True, capture_output=True)
     asm = out.read_text()
     kernels = re.findall(r"^\s+\.amdhsa_kernel\s+(\S+)", asm, re.M)
