@@ -7,8 +7,8 @@ One step = one pass of the whole scan path over both full-size databases:
     D0=D1=1024): a B=1 query (m=2) and a B=16 batch (m=32) sharing the tiled DB;
   * scalar-HE, 64 GiB int8 DB (M=K=262144): a B=1 query and a B=32 batch.
 
-The tiled RowSel DB is built once by pirscan_layout_db before timing (the DB
-is static).  All inputs are seeded synthetic data resident in HBM before the
+The tiled RowSel DB is built once by pirscan_layout_db and the tiled scalar DB
+by pirscan_scalar_layout_db before timing (the databases are static).  All inputs are seeded synthetic data resident in HBM before the
 timed region.  ``value`` = DB bytes scanned per step / step time (GB/s,
 1 GB = 1e9 B).  Per-scan times come from HIP events on the stream the kernels
 run on: around each scan call, and -- through the library's kernel-timer hook
@@ -142,12 +142,20 @@ class Workloads:
         log("setup: scalar 64 GiB DB")
         self.sdb = torch.empty((SC_M, SC_K), dtype=torch.int8, device=dev)
         synth.fill_int8_(self.sdb, SEEDS["scalar"], synth.STREAM_SCALAR_DB)
+        # the static DB is tiled once for the scan (the row-major bytes stay for
+        # the other aspect ratios, which use the row-major entry point)
+        self.sdbt = torch.empty(pirscan.scalar_layout_db_bytes(SC_M, SC_K), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pirscan.scalar_layout_db(self.sdb, self.sdbt)
+        torch.cuda.synchronize()
+        self.slayout_s = time.perf_counter() - t0
         self.q, self.sout, self.ws = {}, {}, {}
         for B in (1, 32):
             self.q[B] = torch.empty((SC_K, B), dtype=torch.int32, device=dev)
             synth.fill_uint32_(self.q[B], SEEDS["scalar"], synth.STREAM_SCALAR_Q)
             self.sout[B] = torch.empty((SC_M, B), dtype=torch.int32, device=dev)
-            self.ws[B] = torch.empty(pirscan.scalar_workspace_bytes(SC_M, SC_K, B), dtype=torch.uint8,
+            self.ws[B] = torch.empty(pirscan.scalar_tiled_workspace_bytes(SC_M, SC_K, B), dtype=torch.uint8,
                                      device=dev)
         log("setup: ExpPack 15 GiB hint (synthesise p-major, one-time relayout)")
         self.eshape = pirscan.ExppackShape.make(RS_N, RS_Q, EP_DR, EP_N)
@@ -239,7 +247,7 @@ class Workloads:
         for B in (1, 32):
             q, o, ws = self.q[B], self.sout[B], self.ws[B]
             out[f"scalar_64GiB_B{B}"] = (
-                (lambda q=q, o=o, ws=ws: pz.scalar_gemm_u32(self.sdb, q, o, ws)),
+                (lambda q=q, o=o, ws=ws: pz.scalar_gemm_u32_tiled(self.sdbt, SC_M, SC_K, q, o, ws)),
                 sc_db, sc_db + 4 * SC_K * B + 4 * SC_M * B, B, SC_M * SC_K * B, "scalar")
         return out
 
@@ -259,10 +267,10 @@ class Workloads:
         return out
 
 
-# int8 MACs the MFMA paths issue per algorithmic MAC: the scalar B>1 GEMM
-# multiplies 4 query digit planes; RowSel / ExpPack multiply 4 x 4 limb pairs,
+# int8 MACs the MFMA paths issue per algorithmic MAC: the scalar GEMM
+# multiplies 4 query digit planes (B = 1 pads each plane to a 16-column tile); RowSel / ExpPack multiply 4 x 4 limb pairs,
 # and at m = 2 pad the 2 rows to a 16-row tile (x 8).
-MFMA_MACS_PER_MAC = {"rowsel_48GiB_B1": 128, "rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4,
+MFMA_MACS_PER_MAC = {"rowsel_48GiB_B1": 128, "rowsel_48GiB_B16": 16, "scalar_64GiB_B1": 64, "scalar_64GiB_B32": 4,
                      "exppack_15GiB_B1": 128, "exppack_15GiB_B16": 16,
                      **{name: 4 for name, (M, K, B) in SHAPE_SCANS.items() if B > 1}}
 # shapes whose int8 MFMA work exceeds what HBM time allows: priced against the MFMA peak
@@ -317,11 +325,11 @@ def traffic_for(name):
 SCAN_KERNELS = {
     "rowsel_48GiB_B1": "rowsel_packed_direct_kernel<1>",
     "rowsel_48GiB_B16": "rowsel_packed_kernel<2, 2",
-    "scalar_64GiB_B1": "gemv_kernel",
-    "scalar_64GiB_B32": "mfma_kernel<8>",
+    "scalar_64GiB_B1": "mfma_kernel<4, true>",
+    "scalar_64GiB_B32": "mfma_kernel<8, true>",
     "exppack_15GiB_B1": "rowsel_packed_direct_kernel<1>",
     "exppack_15GiB_B16": "rowsel_packed_kernel<2, 2",
-    **{name: ("gemv_kernel" if B == 1 else "mfma_kernel<8>") for name, (M, K, B) in SHAPE_SCANS.items()},
+    **{name: ("gemv_kernel" if B == 1 else "mfma_kernel<8, false>") for name, (M, K, B) in SHAPE_SCANS.items()},
     "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
     "ntt_inv_hint": "ntt_kernel<12, true>",
     "ntt_fwd_hint": "ntt_kernel<12, false>",
@@ -633,7 +641,7 @@ def main():
                               "D0": RS_D0, "D1": RS_D1, "m": [2, 32]},
                    "scalar": {"M": SC_M, "K": SC_K, "B": [1, 32]},
                    "hbm_frac_of_step": value / HBM_PEAK_GBS,
-                   "layout_db_once_ms": w.layout_s * 1e3},
+                   "layout_db_once_ms": w.layout_s * 1e3, "scalar_layout_db_once_ms": w.slayout_s * 1e3},
         "roofline": dict(per[dominant]["roofline"], kernel=SCAN_KERNELS[dominant], scan=dominant),
         "workloads": per,
         "next_rows": {"exppack": {"config": {"N": RS_N, "R": len(RS_Q), "Dr": EP_DR, "n": EP_N, "B": [1, 16],

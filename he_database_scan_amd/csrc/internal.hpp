@@ -134,6 +134,16 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
                          uint64_t K, uint32_t B, const ScalarPlan& plan, void* workspace,
                          hipStream_t stream);
 
+// The tiled scalar DB (pirscan_scalar_layout_db): 16-row tiles x 64-k steps
+// of 1 KiB int8 MFMA A fragments, lane (li, lg) = db[16t + li][64s + 16lg ..
+// +15], zero past M and K.  Every batch size runs the MFMA scan on it.
+uint64_t scalar_layout_bytes(uint64_t M, uint64_t K);
+hipError_t launch_scalar_layout(const int8_t* db, void* dst, uint64_t M, uint64_t K, hipStream_t stream);
+bool scalar_tiled_plan(uint64_t M, uint64_t K, uint32_t B, ScalarPlan* plan);
+hipError_t launch_scalar_tiled(const void* db_tiled, const uint32_t* query, uint32_t* out, uint64_t M,
+                               uint64_t K, uint32_t B, const ScalarPlan& plan, void* workspace,
+                               hipStream_t stream);
+
 // ---- negacyclic NTT over RNS polynomials ------------------------------
 
 struct PsiTable {

@@ -455,6 +455,48 @@ int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* o
       pirscan::launch_scalar(db, query, out, M, K, B, p, workspace, (hipStream_t)stream));
 }
 
+size_t pirscan_scalar_layout_db_bytes(uint64_t M, uint64_t K) {
+  pirscan::ScalarPlan p;
+  if (!pirscan::scalar_tiled_plan(M, K, 1, &p)) return 0;
+  return (size_t)pirscan::scalar_layout_bytes(M, K);
+}
+
+int pirscan_scalar_layout_db(const int8_t* db, void* db_tiled, uint64_t M, uint64_t K, void* stream) {
+  pirscan::ScalarPlan p;
+  if (!db || !db_tiled || !pirscan::scalar_tiled_plan(M, K, 1, &p)) return PIRSCAN_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(db_tiled) % 16) != 0) return PIRSCAN_EINVAL;
+  if (overlap(db, M * K, db_tiled, pirscan::scalar_layout_bytes(M, K))) return PIRSCAN_EINVAL;
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  return device_status(pirscan::launch_scalar_layout(db, db_tiled, M, K, (hipStream_t)stream));
+}
+
+size_t pirscan_scalar_tiled_workspace_bytes(uint64_t M, uint64_t K, uint32_t B) {
+  pirscan::ScalarPlan p;
+  if (!pirscan::scalar_tiled_plan(M, K, B, &p)) return 0;
+  return p.total_bytes;
+}
+
+int pirscan_scalar_gemm_u32_tiled(const void* db_tiled, const uint32_t* query, uint32_t* out, uint64_t M,
+                                  uint64_t K, uint32_t B, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (!db_tiled || !query || !out || !workspace) return PIRSCAN_EINVAL;
+  pirscan::ScalarPlan p;
+  if (!pirscan::scalar_tiled_plan(M, K, B, &p)) return PIRSCAN_EINVAL;
+  const uint64_t db_bytes = pirscan::scalar_layout_bytes(M, K), q_bytes = K * B * 4ull, o_bytes = M * B * 4ull;
+  if ((reinterpret_cast<uintptr_t>(db_tiled) % 16) != 0) return PIRSCAN_EINVAL;
+  if (workspace_bytes < p.total_bytes || (reinterpret_cast<uintptr_t>(workspace) % 16) != 0)
+    return PIRSCAN_EINVAL;
+  if (overlap(workspace, p.total_bytes, db_tiled, db_bytes) || overlap(workspace, p.total_bytes, query, q_bytes) ||
+      overlap(workspace, p.total_bytes, out, o_bytes))
+    return PIRSCAN_EINVAL;
+  if (overlap(out, o_bytes, db_tiled, db_bytes) || overlap(out, o_bytes, query, q_bytes)) return PIRSCAN_EINVAL;
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  return device_status(
+      pirscan::launch_scalar_tiled(db_tiled, query, out, M, K, B, p, workspace, (hipStream_t)stream));
+}
+
 size_t pirscan_ntt_plan_bytes(const pirscan_ntt_shape* s) {
   pirscan::NttDesc d;
   if (!ntt_shape_ok(s, &d)) return 0;

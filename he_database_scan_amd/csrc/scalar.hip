@@ -25,12 +25,15 @@
 //    epilogue recombines the four digit planes with shifts, mod 2^32.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace pirscan {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr uint64_t kScalarGroupTiles = 16;  // row tiles per contiguous group of the tiled DB
 constexpr int kGemvJ = 4;                          // 16-byte loads per lane per row
 constexpr uint64_t kGemvKBlock = 64 * 16 * kGemvJ;  // 4096
 constexpr int kGemvRowsPerWave = 64;
@@ -257,13 +260,15 @@ struct MfmaShape {
 };
 
 // One tile (kb, rb).  Starts and ends with every wave past a barrier, so the
-// LDS buffers are free on entry and on exit.
-template <int NT>
+// LDS buffers are free on entry and on exit.  PACKED: the DB is in the tiled
+// layout of pirscan_scalar_layout_db (16-row tiles x 64-k steps of 1 KiB
+// A fragments, `ptiles` x `psteps` of them, zero-padded), otherwise row-major.
+template <int NT, bool PACKED>
 __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const uint8_t* dig,
                                           uint32_t* __restrict__ dst, uint64_t M, uint64_t K,
                                           uint64_t kblock, uint64_t nkb, uint32_t bgroup, uint64_t ldd,
-                                          uint32_t dcol0, uint64_t kb, uint64_t rb,
-                                          uint8_t (*bsm)[MfmaShape<NT>::CHUNK_BYTES]) {
+                                          uint32_t dcol0, uint64_t kb, uint64_t rb, uint64_t ptiles,
+                                          uint64_t psteps, uint8_t (*bsm)[MfmaShape<NT>::CHUNK_BYTES]) {
   constexpr int HT = MfmaShape<NT>::HT;
   constexpr int DCOLS = MfmaShape<NT>::DCOLS;
   constexpr int CHUNK_BYTES = MfmaShape<NT>::CHUNK_BYTES;
@@ -280,12 +285,32 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
   // A rows past M and k past K are read from clamped (valid) addresses: rows
   // past M are never stored, and k past K meets zero digits.
   const int8_t* arow[kMfmaRowTiles2];
+  const v4i* atile[kMfmaRowTiles2];
 #pragma unroll
   for (int rt = 0; rt < kMfmaRowTiles2; ++rt) {
-    const uint64_t row = row0 + rt * 16 + li;
-    arow[rt] = db + (row < M ? row : M - 1) * K;
+    if constexpr (PACKED) {
+      uint64_t t = (row0 + rt * 16) / 16;
+      t = t < ptiles ? t : ptiles - 1;
+      atile[rt] = reinterpret_cast<const v4i*>(db) +
+                  ((t / kScalarGroupTiles) * psteps * kScalarGroupTiles + t % kScalarGroupTiles) * 64 + lane;
+    } else {
+      const uint64_t row = row0 + rt * 16 + li;
+      arow[rt] = db + (row < M ? row : M - 1) * K;
+    }
   }
   const uint64_t klast = K - 16;  // last valid 16-byte chunk of a row (K % 16 == 0)
+  // A fragment of row tile rt at 64-k step `step` of this k-block
+  auto load_a = [&](int rt, uint32_t step) -> v4i {
+    if constexpr (PACKED) {
+      uint64_t sg = kbeg / 64 + step;
+      sg = sg < psteps ? sg : psteps - 1;
+      return __builtin_nontemporal_load(atile[rt] + sg * (64 * kScalarGroupTiles));
+    } else {
+      uint64_t ko = kbeg + (uint64_t)step * 64 + 16 * lg;
+      ko = ko < klast ? ko : klast;
+      return load_db16_v4i(arow[rt] + ko);
+    }
+  };
 
   // chunk c of this k-block is CHUNK_BYTES contiguous bytes of the digit array
   // (dig is not __restrict__: the compiler barrier below must be able to
@@ -303,12 +328,9 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
   // prologue: A ring for steps 0..depth-1, B chunk 0 into LDS
   v4i a[DEPTH][kMfmaRowTiles2];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    uint64_t ko = kbeg + (uint64_t)d * 64 + 16 * lg;
-    ko = ko < klast ? ko : klast;
+  for (int d = 0; d < DEPTH; ++d)
 #pragma unroll
-    for (int rt = 0; rt < kMfmaRowTiles2; ++rt) a[d][rt] = load_db16_v4i(arow[rt] + ko);
-  }
+    for (int rt = 0; rt < kMfmaRowTiles2; ++rt) a[d][rt] = load_a(rt, d);
   {
     u32x4 breg[PIECES];
 #pragma unroll
@@ -358,14 +380,10 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
             // cannot sink the digit-chunk loads down to their LDS store.
             uint32_t nxt = step - 1 + DEPTH;
             nxt = nxt < nsteps ? nxt : nsteps - 2;
-            uint64_t ko0 = kbeg + (uint64_t)nxt * 64 + 16 * lg;
-            uint64_t ko1 = ko0 + 64;
-            ko0 = ko0 < klast ? ko0 : klast;
-            ko1 = ko1 < klast ? ko1 : klast;
 #pragma unroll
             for (int rt = 0; rt < kMfmaRowTiles2; ++rt) {
-              a[slot - 1][rt] = load_db16_v4i(arow[rt] + ko0);
-              a[slot][rt] = load_db16_v4i(arow[rt] + ko1);
+              a[slot - 1][rt] = load_a(rt, nxt);
+              a[slot][rt] = load_a(rt, nxt + 1);
             }
             // keep the refill here: the scheduler would otherwise sink it
             // next to its use (to save registers) and undo the prefetch
@@ -403,13 +421,14 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
   }
 }
 
-template <int NT>
+template <int NT, bool PACKED>
 __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(const int8_t* __restrict__ db,
                                                                const uint8_t* dig,
                                                                uint32_t* __restrict__ dst, uint64_t M,
                                                                uint64_t K, uint64_t kblock, uint64_t nkb,
                                                                uint64_t row_blocks, uint32_t bgroup,
-                                                               uint64_t ldd, uint32_t dcol0) {
+                                                               uint64_t ldd, uint32_t dcol0, uint64_t ptiles,
+                                                               uint64_t psteps) {
   __shared__ __attribute__((aligned(16))) uint8_t bsm[2][MfmaShape<NT>::CHUNK_BYTES];
   constexpr uint32_t kXcds = 8;
   const uint32_t hw = blockIdx.x, G = gridDim.x;  // G >= kXcds (host guarantees)
@@ -418,7 +437,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(const int8_t* __r
   const uint64_t tiles = nkb * row_blocks;
   const uint64_t lo = tiles * xcd / kXcds, hi = tiles * (xcd + 1) / kXcds;
   for (uint64_t t = lo + j; t < hi; t += per_xcd)
-    mfma_tile<NT>(db, dig, dst, M, K, kblock, nkb, bgroup, ldd, dcol0, t / row_blocks, t % row_blocks, bsm);
+    mfma_tile<NT, PACKED>(db, dig, dst, M, K, kblock, nkb, bgroup, ldd, dcol0, t / row_blocks, t % row_blocks,
+                          ptiles, psteps, bsm);
 }
 
 // ---------------------------------------------------------------------------
@@ -466,7 +486,7 @@ uint32_t grid_for(uint64_t items, uint64_t cap = 1u << 20) {
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 uint64_t align_up(uint64_t a, uint64_t b) { return ceil_div(a, b) * b; }
 
-template <int NT>
+template <int NT, bool PACKED>
 hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint64_t M, uint64_t K,
                        const ScalarPlan& pl, uint32_t bgroup, uint64_t ldd, uint32_t dcol0,
                        hipStream_t stream) {
@@ -477,15 +497,190 @@ hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<NT>, 64 * kMfmaWaves, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<NT, PACKED>, 64 * kMfmaWaves, 0);
   if (e != hipSuccess) return e;
   // persistent: as many workgroups as are co-resident, at least one per XCD
   uint64_t grid = (uint64_t)cus * (uint64_t)(per_cu > 0 ? per_cu : 1);
   if (grid > row_blocks * pl.nkb) grid = row_blocks * pl.nkb;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL((mfma_kernel<NT>), dim3((uint32_t)grid), dim3(64 * kMfmaWaves), 0, stream, db, dig,
-                     dst, M, K, pl.kblock, pl.nkb, row_blocks, bgroup, ldd, dcol0);
+  hipLaunchKernelGGL((mfma_kernel<NT, PACKED>), dim3((uint32_t)grid), dim3(64 * kMfmaWaves), 0, stream, db,
+                     dig, dst, M, K, pl.kblock, pl.nkb, row_blocks, bgroup, ldd, dcol0,
+                     ceil_div(M, 16 * kScalarGroupTiles) * kScalarGroupTiles, ceil_div(K, 64));
   return hipGetLastError();
+}
+
+// B == 1 on the tiled DB: GEMV with packed int8 dot products.  A wavefront
+// owns TG row tiles (16 TG rows) of one k-block; per 64-k step it loads the
+// TG 1 KiB fragments (lane (li, lg): row li, k = 64s + 16lg + 0..15) one step
+// ahead, and the 64 bytes of digits of its 16 k (the GEMV digit layout: per
+// 4-k group, one dword per plane), the same address for the 16 lanes of a
+// k-group.  Each DB dword meets its 4 digit dwords in 4 v_dot4_i32_i8 (int32
+// wrap-around = mod 2^32); the planes are recombined with shifts and the 4
+// k-groups of a row summed across lanes at the end.
+#ifndef PIRSCAN_TGEMV_TILES
+#define PIRSCAN_TGEMV_TILES 4
+#endif
+#ifndef PIRSCAN_TGEMV_WAVES
+#define PIRSCAN_TGEMV_WAVES 4096
+#endif
+#ifndef PIRSCAN_TGEMV_RING
+#define PIRSCAN_TGEMV_RING 2
+#endif
+constexpr int kTiledGemvTiles = PIRSCAN_TGEMV_TILES;
+constexpr int kTiledGemvRing = PIRSCAN_TGEMV_RING;
+constexpr uint64_t kTiledGemvTargetWaves = PIRSCAN_TGEMV_WAVES;  // 4 per SIMD
+__global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const u32x4* __restrict__ dbp,
+                                                              const u32x4* __restrict__ dig,
+                                                              uint32_t* __restrict__ dst, uint64_t M,
+                                                              uint64_t ptiles, uint64_t psteps,
+                                                              uint64_t kblock_steps, uint64_t nkb,
+                                                              uint64_t items) {
+  constexpr int TG = kTiledGemvTiles;
+  const uint32_t lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t li = lane % 16, lg = lane / 16;
+  const uint64_t item = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
+  if (item >= items) return;  // no barriers in this kernel
+  const uint64_t kb = item % nkb, tg = item / nkb;
+  const uint64_t s0 = kb * kblock_steps;
+  const uint64_t nst = (s0 + kblock_steps < psteps ? s0 + kblock_steps : psteps) - s0;  // >= 1
+  const u32x4* frag[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    uint64_t tile = tg * TG + t;
+    tile = tile < ptiles ? tile : ptiles - 1;
+    frag[t] = dbp + ((tile / kScalarGroupTiles * psteps + s0) * kScalarGroupTiles + tile % kScalarGroupTiles) * 64 +
+              lane;
+  }
+  const u32x4* dg = dig + s0 * 16 + 4 * lg;  // per step: 16 groups of 4 k, 4 of them this lane's
+
+  int acc[TG][4];
+#pragma unroll
+  for (int t = 0; t < TG; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[t][j] = 0;
+  // ring of kRingG steps, loads kRingG - 1 steps ahead; the step count is
+  // rounded up to whole ring turns, the extra steps reading a reloaded DB
+  // fragment against the zero digits past the array's last real step
+  constexpr int R = kTiledGemvRing;
+  u32x4 a[R][TG], d[R][4];
+  const u32x4* dzero = dig + psteps * 16 + 4 * lg;
+  auto load = [&](int slot, uint64_t s) {
+    const uint64_t ss = s < nst ? s : nst - 1;
+#pragma unroll
+    for (int t = 0; t < TG; ++t) a[slot][t] = __builtin_nontemporal_load(frag[t] + ss * (64 * kScalarGroupTiles));
+    const u32x4* ds = s < nst ? dg + s * 16 : dzero;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[slot][u] = ds[u];
+  };
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r) load(r, r);
+  for (uint64_t s = 0; s < nst; s += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      load((r + R - 1) % R, s + r + R - 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        const uint32_t w[4] = {a[r][t].x, a[r][t].y, a[r][t].z, a[r][t].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t dj[4] = {d[r][u].x, d[r][u].y, d[r][u].z, d[r][u].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[t][j] = __builtin_amdgcn_sdot4((int)w[u], (int)dj[j], acc[t][j], false);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    uint32_t v = (uint32_t)acc[t][0] + ((uint32_t)acc[t][1] << 8) + ((uint32_t)acc[t][2] << 16) +
+                 ((uint32_t)acc[t][3] << 24);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    const uint64_t row = (tg * TG + t) * 16 + li;
+    if (lg == 0 && row < M) dst[kb * M + row] = v;
+  }
+}
+
+// The MFMA passes of up to kMfmaMaxCols query columns: digit split, scan,
+// split-K reduction.
+template <bool PACKED>
+hipError_t run_mfma_passes(const int8_t* db, const uint32_t* query, uint32_t* out, uint64_t M, uint64_t K,
+                           uint32_t B, const ScalarPlan& pl, uint8_t* dig, uint32_t* part, hipStream_t stream) {
+  hipError_t e;
+  for (uint32_t c0 = 0; c0 < B; c0 += pl.bgroup) {
+    const uint32_t bg = (B - c0) < pl.bgroup ? (B - c0) : pl.bgroup;
+    const uint32_t bpad = (uint32_t)align_up(bg, 16);
+    const uint64_t k16 = pl.kpad / 16;
+    hipLaunchKernelGGL(split_mfma_kernel, dim3(grid_for(k16 * bpad)), dim3(kThreads), 0, stream, query,
+                       dig, K, k16, bpad, bg, B, c0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint32_t* dst = pl.nkb > 1 ? part : out;
+    timer_mark_start(stream);  // first pass only
+    switch (bpad) {
+      case 16: e = launch_mfma<4, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+      case 32: e = launch_mfma<8, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+      case 48: e = launch_mfma<12, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+      default: e = launch_mfma<16, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+    }
+    if (e != hipSuccess) return e;
+    if (c0 + pl.bgroup >= B) timer_mark_stop(stream);  // last pass: before its reduction
+    if (pl.nkb > 1) {
+      hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M * bg)), dim3(kThreads), 0, stream, part, out, M,
+                         bg, pl.nkb, (uint64_t)B, c0);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+// MFMA plan: up to kMfmaMaxCols columns per pass, K split only as far as the
+// tiles must be to fill the GPU.
+void mfma_plan(uint64_t M, uint64_t K, uint32_t B, ScalarPlan* p) {
+  p->mfma = true;
+  p->bgroup = B < kMfmaMaxCols ? B : kMfmaMaxCols;
+  p->bpad = (uint32_t)align_up(p->bgroup, 16);
+  const uint64_t row_blocks = ceil_div(M, (uint64_t)kMfmaWaves * 16 * kMfmaRowTiles2);
+  uint64_t nkb = ceil_div(kMfmaTargetTiles, row_blocks);
+  const uint64_t chunks = ceil_div(K, kMfmaChunkK);
+  if (nkb > chunks) nkb = chunks;
+  p->kblock = align_up(ceil_div(K, nkb), kMfmaChunkK);
+  p->nkb = ceil_div(K, p->kblock);
+  p->kpad = p->nkb * p->kblock;
+  p->digit_bytes = p->kpad * 4 * p->bpad;
+  p->part_bytes = p->nkb > 1 ? p->nkb * M * p->bgroup * 4 : 0;
+  p->total_bytes = align_up(p->digit_bytes, 256) + p->part_bytes;
+}
+
+// Tiled scalar DB: 16-byte lane (li, lg) of (row tile T, 64-k step s) holds
+// db[16T + li][64s + 16lg + 0..15], zero past M and K; one thread per lane.
+// Fragment order [T / 16][s][T % 16][lane]: a group of 16 row tiles (the
+// tiles of one workgroup) is one contiguous run, step after step.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void pack_scalar_kernel(const int8_t* __restrict__ db,
+                                                               uint4* __restrict__ dst, uint64_t M,
+                                                               uint64_t K, uint64_t steps, uint64_t total) {
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t e = (uint64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const uint32_t lane = (uint32_t)(e % 64);
+    const uint64_t f = e / 64, tl = f % kScalarGroupTiles, gs = f / kScalarGroupTiles;
+    const uint64_t s = gs % steps, t = (gs / steps) * kScalarGroupTiles + tl;
+    const uint64_t row = t * 16 + lane % 16, k0 = s * 64 + (lane / 16) * 16;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < M && k0 < K) {
+      const int8_t* src = db + row * K + k0;
+      if (VEC) {  // K % 16 == 0: the 16 bytes are all inside the row
+        v = *reinterpret_cast<const uint4*>(src);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+        for (uint32_t i = 0; i < 16 && k0 + i < K; ++i) w[i / 4] |= (uint32_t)(uint8_t)src[i] << (8 * (i % 4));
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    dst[e] = v;
+  }
 }
 
 }  // namespace
@@ -509,21 +704,10 @@ bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPl
     p->kpad = p->nkb * p->kblock;
     p->digit_bytes = p->kpad * 4;  // 4 digit planes x 1 byte per k
     p->part_bytes = p->nkb > 1 ? p->nkb * M * 4 : 0;
+    p->total_bytes = align_up(p->digit_bytes, 256) + p->part_bytes;
   } else {
-    p->mfma = true;
-    p->bgroup = B < kMfmaMaxCols ? B : kMfmaMaxCols;
-    p->bpad = (uint32_t)align_up(p->bgroup, 16);
-    const uint64_t row_blocks = ceil_div(M, (uint64_t)kMfmaWaves * 16 * kMfmaRowTiles2);
-    uint64_t nkb = ceil_div(kMfmaTargetTiles, row_blocks);
-    const uint64_t chunks = ceil_div(K, kMfmaChunkK);
-    if (nkb > chunks) nkb = chunks;
-    p->kblock = align_up(ceil_div(K, nkb), kMfmaChunkK);
-    p->nkb = ceil_div(K, p->kblock);
-    p->kpad = p->nkb * p->kblock;
-    p->digit_bytes = p->kpad * 4 * p->bpad;
-    p->part_bytes = p->nkb > 1 ? p->nkb * M * p->bgroup * 4 : 0;
+    mfma_plan(M, K, B, p);
   }
-  p->total_bytes = align_up(p->digit_bytes, 256) + p->part_bytes;
   return true;
 }
 
@@ -562,29 +746,81 @@ hipError_t launch_scalar(const int8_t* db, const uint32_t* query, uint32_t* out,
     }
     return hipSuccess;
   }
-  uint8_t* dig = ws;
-  for (uint32_t c0 = 0; c0 < B; c0 += pl.bgroup) {
-    const uint32_t bg = (B - c0) < pl.bgroup ? (B - c0) : pl.bgroup;
-    const uint32_t bpad = (uint32_t)align_up(bg, 16);
-    const uint64_t k16 = pl.kpad / 16;
-    hipLaunchKernelGGL(split_mfma_kernel, dim3(grid_for(k16 * bpad)), dim3(kThreads), 0, stream, query,
-                       dig, K, k16, bpad, bg, B, c0);
+  return run_mfma_passes<false>(db, query, out, M, K, B, pl, ws, part, stream);
+}
+
+bool scalar_tiled_plan(uint64_t M, uint64_t K, uint32_t B, ScalarPlan* p) {
+  *p = ScalarPlan{};
+  if (M == 0 || K == 0 || B == 0 || B > (1u << 20)) return false;
+  const unsigned __int128 lim = (unsigned __int128)1 << 62;
+  if ((unsigned __int128)M * K > lim || (unsigned __int128)M * B * 4 > lim ||
+      (unsigned __int128)K * B * 4 > lim)
+    return false;
+  p->fast = true;
+  if (B > 1) {
+    mfma_plan(M, K, B, p);
+    return true;
+  }
+  // B == 1: GEMV over wavefronts of kTiledGemvTiles row tiles, K split into
+  // whole 64-k steps until there are enough wavefronts to fill the GPU
+  p->mfma = false;
+  p->bgroup = 1;
+  p->bpad = 1;
+  const uint64_t psteps = ceil_div(K, 64);
+  const uint64_t waves = ceil_div(ceil_div(M, 16), kTiledGemvTiles);
+  uint64_t nkb = ceil_div(kTiledGemvTargetWaves, waves);
+  if (nkb > psteps) nkb = psteps;
+  p->kblock = ceil_div(psteps, nkb) * 64;
+  p->nkb = ceil_div(psteps * 64, p->kblock);
+  p->kpad = (psteps + 1) * 64;  // one step of zero digits past the last (the ring's padding steps)
+  p->digit_bytes = p->kpad * 4;
+  p->part_bytes = p->nkb > 1 ? p->nkb * M * 4 : 0;
+  p->total_bytes = align_up(p->digit_bytes, 256) + p->part_bytes;
+  return true;
+}
+
+uint64_t scalar_layout_bytes(uint64_t M, uint64_t K) {
+  return ceil_div(M, 16 * kScalarGroupTiles) * kScalarGroupTiles * ceil_div(K, 64) * 1024;
+}
+
+hipError_t launch_scalar_layout(const int8_t* db, void* dst, uint64_t M, uint64_t K, hipStream_t stream) {
+  const uint64_t total = scalar_layout_bytes(M, K) / 16;
+  const bool vec = K % 16 == 0 && reinterpret_cast<uintptr_t>(db) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL((pack_scalar_kernel<true>), dim3(grid_for(total)), dim3(kThreads), 0, stream, db,
+                       static_cast<uint4*>(dst), M, K, ceil_div(K, 64), total);
+  else
+    hipLaunchKernelGGL((pack_scalar_kernel<false>), dim3(grid_for(total)), dim3(kThreads), 0, stream, db,
+                       static_cast<uint4*>(dst), M, K, ceil_div(K, 64), total);
+  return hipGetLastError();
+}
+
+hipError_t launch_scalar_tiled(const void* db_tiled, const uint32_t* query, uint32_t* out, uint64_t M,
+                               uint64_t K, uint32_t B, const ScalarPlan& pl, void* workspace,
+                               hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* part = reinterpret_cast<uint32_t*>(ws + align_up(pl.digit_bytes, 256));
+  if (pl.mfma)
+    return run_mfma_passes<true>(static_cast<const int8_t*>(db_tiled), query, out, M, K, B, pl, ws, part, stream);
+  hipError_t e;
+  const uint64_t groups = pl.kpad / 4;
+  hipLaunchKernelGGL(split_gemv_kernel, dim3(grid_for(groups)), dim3(kThreads), 0, stream, query,
+                     reinterpret_cast<uint32_t*>(ws), K, groups, 1u, 0u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const uint64_t ptiles = ceil_div(M, 16 * kScalarGroupTiles) * kScalarGroupTiles, psteps = ceil_div(K, 64);
+  const uint64_t items = ceil_div(ptiles, kTiledGemvTiles) * pl.nkb, grid = ceil_div(items, 4);
+  if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  uint32_t* dst = pl.nkb > 1 ? part : out;
+  timer_mark_start(stream);
+  hipLaunchKernelGGL(gemv_tiled_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(db_tiled), reinterpret_cast<const u32x4*>(ws), dst, M, ptiles, psteps,
+                     pl.kblock / 64, pl.nkb, items);
+  timer_mark_stop(stream);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (pl.nkb > 1) {
+    hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M)), dim3(kThreads), 0, stream, part, out, M, 1u, pl.nkb,
+                       1ull, 0u);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    uint32_t* dst = pl.nkb > 1 ? part : out;
-    timer_mark_start(stream);  // first pass only
-    switch (bpad) {
-      case 16: e = launch_mfma<4>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
-      case 32: e = launch_mfma<8>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
-      case 48: e = launch_mfma<12>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
-      default: e = launch_mfma<16>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
-    }
-    if (e != hipSuccess) return e;
-    if (c0 + pl.bgroup >= B) timer_mark_stop(stream);  // last pass: before its reduction
-    if (pl.nkb > 1) {
-      hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M * bg)), dim3(kThreads), 0, stream, part, out, M,
-                         bg, pl.nkb, (uint64_t)B, c0);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
   }
   return hipSuccess;
 }

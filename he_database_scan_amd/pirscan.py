@@ -142,6 +142,14 @@ def _load():
         L.pirscan_scalar_workspace_bytes.restype = sz
         L.pirscan_scalar_gemm_u32.argtypes = [vp, vp, vp, u64, u64, u32, vp, sz, vp]
         L.pirscan_scalar_gemm_u32.restype = ctypes.c_int
+        L.pirscan_scalar_layout_db_bytes.argtypes = [u64, u64]
+        L.pirscan_scalar_layout_db_bytes.restype = sz
+        L.pirscan_scalar_layout_db.argtypes = [vp, vp, u64, u64, vp]
+        L.pirscan_scalar_layout_db.restype = ctypes.c_int
+        L.pirscan_scalar_tiled_workspace_bytes.argtypes = [u64, u64, u32]
+        L.pirscan_scalar_tiled_workspace_bytes.restype = sz
+        L.pirscan_scalar_gemm_u32_tiled.argtypes = [vp, vp, vp, u64, u64, u32, vp, sz, vp]
+        L.pirscan_scalar_gemm_u32_tiled.restype = ctypes.c_int
         nsp = ctypes.POINTER(NttShape)
         L.pirscan_ntt_plan_bytes.argtypes = [nsp]
         L.pirscan_ntt_plan_bytes.restype = sz
@@ -309,6 +317,40 @@ def scalar_gemm_u32(db, query, out, workspace=None, stream=None) -> None:
            _load().pirscan_scalar_gemm_u32(_ptr(db), _ptr(query), _ptr(out), M, K, B,
                                            _ptr(workspace) if need else ctypes.c_void_p(0),
                                            wbytes, _stream(stream)))
+
+
+def scalar_layout_db_bytes(M: int, K: int) -> int:
+    return int(_load().pirscan_scalar_layout_db_bytes(M, K))
+
+
+def scalar_layout_db(db, db_tiled, stream=None) -> None:
+    """db [M][K] int8 (row-major) -> db_tiled, a device buffer of at least
+    ``scalar_layout_db_bytes(M, K)`` bytes (any dtype)."""
+    M, K = db.shape
+    _dev(db, "db", 1, M * K)
+    _dev_bytes(db_tiled, "db_tiled", scalar_layout_db_bytes(M, K))
+    _check("pirscan_scalar_layout_db",
+           _load().pirscan_scalar_layout_db(_ptr(db), _ptr(db_tiled), M, K, _stream(stream)))
+
+
+def scalar_tiled_workspace_bytes(M: int, K: int, B: int) -> int:
+    return int(_load().pirscan_scalar_tiled_workspace_bytes(M, K, B))
+
+
+def scalar_gemm_u32_tiled(db_tiled, M: int, K: int, query, out, workspace, stream=None) -> None:
+    """out[M][B] = sext(db) @ query[K][B] mod 2^32 on the tiled DB, on device.
+
+    ``workspace``: at least ``scalar_tiled_workspace_bytes(M, K, B)`` bytes,
+    owned by the caller.
+    """
+    B = query.shape[1] if query.dim() == 2 else 1
+    _dev_bytes(db_tiled, "db_tiled", scalar_layout_db_bytes(M, K))
+    _dev(query, "query", 4, K * B)
+    _dev(out, "out", 4, M * B)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check("pirscan_scalar_gemm_u32_tiled",
+           _load().pirscan_scalar_gemm_u32_tiled(_ptr(db_tiled), _ptr(query), _ptr(out), M, K, B,
+                                                 _ptr(workspace), wbytes, _stream(stream)))
 
 
 def ntt_plan_bytes(shape: NttShape) -> int:

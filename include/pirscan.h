@@ -218,6 +218,40 @@ int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* o
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Tiled scalar database.  The DB is static (VIPIR section 2.5: the server
+ * holds it and every query multiplies it), so it can be laid out once in the
+ * order the scans read it: 16-row tiles x 64-byte k steps, 1 KiB per
+ * (tile, step), in groups of 16 tiles whose fragments follow each other step
+ * after step -- a workgroup then streams one contiguous range instead of
+ * 64-byte pieces of 256 different rows.
+ * pirscan_scalar_layout_db_bytes: ceil(M/256) * 16 * ceil(K/64) * 1024 (zero
+ * bytes pad M to 256 and K to 64), 0 on invalid sizes.
+ * pirscan_scalar_layout_db: db [M][K] int8 row-major (any alignment) ->
+ * db_tiled (device memory of that many bytes, 16-byte aligned, opaque, must
+ * not overlap db).  Pure permutation of bytes plus zero padding.
+ */
+size_t pirscan_scalar_layout_db_bytes(uint64_t M, uint64_t K);
+int pirscan_scalar_layout_db(const int8_t* db, void* db_tiled, uint64_t M, uint64_t K, void* stream);
+/* Workspace bytes pirscan_scalar_gemm_u32_tiled needs for (M, K, B): the
+ * signed digit planes of up to 64 query columns plus split-K partial sums.
+ * 0 on invalid sizes. */
+size_t pirscan_scalar_tiled_workspace_bytes(uint64_t M, uint64_t K, uint32_t B);
+/*
+ * The scalar-HE product on the tiled DB: the same result as
+ * pirscan_scalar_gemm_u32 (out[i][b] = sum_k sext32(db[i][k]) * query[k][b]
+ * mod 2^32): B = 1 with packed int8 dot products (v_dot4) against the four
+ * digit planes, B > 1 on int8 MFMA over them.
+ *   db_tiled  : output of pirscan_scalar_layout_db for the same M, K.
+ *   query, out: as for pirscan_scalar_gemm_u32.
+ *   workspace : >= pirscan_scalar_tiled_workspace_bytes(M, K, B) bytes,
+ *               16-byte aligned, caller-owned; contents ignored on entry.
+ * `out` and `workspace` must not overlap db_tiled, query or each other.
+ */
+int pirscan_scalar_gemm_u32_tiled(const void* db_tiled, const uint32_t* query, uint32_t* out,
+                                  uint64_t M, uint64_t K, uint32_t B,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Negacyclic NTT over RNS polynomials -- the transform on either side of the
  * scans: it takes first-step outputs and the hint into the point-wise domain
  * that ExpPack's GEMM consumes (VIPIR section 3.5.2), the plaintext DB into

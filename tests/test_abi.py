@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("pirscan_layout_db", "pirscan_rowsel_modgemm", "pirscan_rowsel_workspace_bytes",
-                 "pirscan_scalar_gemm_u32",
+                 "pirscan_scalar_gemm_u32", "pirscan_scalar_layout_db", "pirscan_scalar_layout_db_bytes",
+                 "pirscan_scalar_tiled_workspace_bytes", "pirscan_scalar_gemm_u32_tiled",
                  "pirscan_scalar_workspace_bytes", "pirscan_layout_db_bytes", "pirscan_strerror",
                  "pirscan_exppack_layout_h", "pirscan_exppack_layout_h_bytes",
                  "pirscan_exppack_workspace_bytes", "pirscan_exppack_modgemm",
@@ -103,6 +104,34 @@ def test_rowsel_workspace_sizes():
     assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(16, Q3, 20000, 64), 32) == 4 * 48 * 32 * 64
     assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(1, [7], 1, 1), 1) == 256 + 256
     assert pirscan.rowsel_workspace_bytes(s, 0) == 0
+
+
+def test_scalar_tiled_sizes_and_validation():
+    # groups of 16 row tiles of 16 rows x 64-byte steps of 1 KiB, zero-padded
+    assert pirscan.scalar_layout_db_bytes(262144, 262144) == 1 << 36
+    assert pirscan.scalar_layout_db_bytes(17, 65) == 16 * 2 * 1024
+    assert pirscan.scalar_layout_db_bytes(257, 64) == 2 * 16 * 1024
+    assert pirscan.scalar_layout_db_bytes(1, 1) == 16 * 1024
+    assert pirscan.scalar_layout_db_bytes(0, 5) == 0 and pirscan.scalar_layout_db_bytes(5, 0) == 0
+    # B > 1: the MFMA plan's digit planes of up to 64 columns and split-K
+    # partials; B = 1: 4 digit bytes per k (and one 64-k step of zeros), K
+    # split while the row tiles are too few to fill the GPU (4096 wavefronts
+    # of 4 tiles)
+    assert pirscan.scalar_tiled_workspace_bytes(262144, 262144, 32) == 262144 * 128
+    assert pirscan.scalar_tiled_workspace_bytes(262144, 262144, 1) == (262144 + 64) * 4   # + one zero step
+    assert pirscan.scalar_tiled_workspace_bytes(32768, 32768, 1) == (32768 + 64) * 4 + 8 * 32768 * 4
+    assert pirscan.scalar_tiled_workspace_bytes(0, 16, 1) == 0
+    L = pirscan.lib()
+    A = 1 << 40   # never dereferenced: every call below fails validation first
+    vp = ctypes.c_void_p
+    # misaligned tiled DB, too small a workspace, overlaps
+    assert L.pirscan_scalar_layout_db(vp(A), vp(A + (1 << 30) + 8), 64, 64, None) == pirscan.EINVAL
+    assert L.pirscan_scalar_layout_db(vp(A), vp(A + 1024), 64, 64, None) == pirscan.EINVAL
+    need = pirscan.scalar_tiled_workspace_bytes(64, 64, 2)
+    f = L.pirscan_scalar_gemm_u32_tiled
+    assert f(vp(A), vp(A + 8192), vp(A + 16384), 64, 64, 2, vp(A + 32768), need - 1, None) == pirscan.EINVAL
+    assert f(vp(A + 8), vp(A + 8192), vp(A + 16384), 64, 64, 2, vp(A + 32768), need, None) == pirscan.EINVAL
+    assert f(vp(A), vp(A + 8192), vp(A), 64, 64, 2, vp(A + 32768), need, None) == pirscan.EINVAL
 
 
 def test_scalar_workspace_sizes():
