@@ -267,10 +267,10 @@ class Workloads:
         return out
 
 
-# int8 MACs the MFMA paths issue per algorithmic MAC: the scalar GEMM
-# multiplies 4 query digit planes (B = 1 pads each plane to a 16-column tile); RowSel / ExpPack multiply 4 x 4 limb pairs,
+# int8 MACs the MFMA paths issue per algorithmic MAC: the scalar B>1 GEMM
+# multiplies 4 query digit planes; RowSel / ExpPack multiply 4 x 4 limb pairs,
 # and at m = 2 pad the 2 rows to a 16-row tile (x 8).
-MFMA_MACS_PER_MAC = {"rowsel_48GiB_B1": 128, "rowsel_48GiB_B16": 16, "scalar_64GiB_B1": 64, "scalar_64GiB_B32": 4,
+MFMA_MACS_PER_MAC = {"rowsel_48GiB_B1": 128, "rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4,
                      "exppack_15GiB_B1": 128, "exppack_15GiB_B16": 16,
                      **{name: 4 for name, (M, K, B) in SHAPE_SCANS.items() if B > 1}}
 # shapes whose int8 MFMA work exceeds what HBM time allows: priced against the MFMA peak
@@ -325,7 +325,7 @@ def traffic_for(name):
 SCAN_KERNELS = {
     "rowsel_48GiB_B1": "rowsel_packed_direct_kernel<1>",
     "rowsel_48GiB_B16": "rowsel_packed_kernel<2, 2",
-    "scalar_64GiB_B1": "mfma_kernel<4, true>",
+    "scalar_64GiB_B1": "gemv_tiled_kernel",
     "scalar_64GiB_B32": "mfma_kernel<8, true>",
     "exppack_15GiB_B1": "rowsel_packed_direct_kernel<1>",
     "exppack_15GiB_B16": "rowsel_packed_kernel<2, 2",

@@ -80,23 +80,25 @@ hipError_t launch_out_relayout(const RowselLaunch& a, const uint32_t* out_t, hip
 // shapes keep the [P][D0][D1] layout and the VALU scan.
 constexpr uint32_t kPackedMaxD0 = 16384;
 bool rowsel_packed_ok(const uint32_t* q, uint32_t R, uint32_t D0);
-// Bytes of the packed operand: per point ceil(D1/16) x ceil(D0/64) x 4 KiB.
+// Bytes of the packed operand: per point ceil(D1/16) column tiles (rounded up
+// to a whole group of tiles) x ceil(D0/64) steps x 4 KiB.
 uint64_t packed_layout_bytes(uint64_t P, uint32_t D0, uint32_t D1);
 
 // Limb packing of a p-major operand into MFMA fragments.  Source word
 // (row, k, p) at src[row * s_row + k * s_k + p] (rows row_base .. rows-1,
 // k < K); the 16 bytes of fragment lane (li, lg) of (p, t, s, limb j) at
-// dst[p * d_p + t * d_t + s * d_s + (4 j + lg) * lpg + li] (strides in
-// 16-byte units) for li < lpg, holding limb j of the centred residues of row
+// dst[p * d_p + (t / tgroup) * d_g + (t % tgroup) * d_t + s * d_s +
+// (4 j + lg) * lpg + li] (strides in 16-byte units) for li < lpg, holding limb j of the centred residues of row
 // row_base + 16t + li at k = 64s + 16lg + 0..15; zero past rows / K.  With
 // lpg = 16 a fragment is 1 KiB of contiguous lanes.
 struct PackDesc {
   const uint32_t* src;
   void* dst;
   uint64_t P, s_row, s_k;
-  uint64_t d_p, d_t, d_s;
+  uint64_t d_p, d_g, d_t, d_s;
   uint32_t N, rows, row_base, K, tiles, S;
-  uint32_t lpg;  // lanes stored per k-group (16, or the live rows of a small batch)
+  uint32_t tgroup;  // tiles per group (t / tgroup selects the group)
+  uint32_t lpg;     // lanes stored per k-group (16, or the live rows of a small batch)
   uint32_t q[kMaxLimbs];
 };
 hipError_t launch_pack(const PackDesc& d, hipStream_t stream);

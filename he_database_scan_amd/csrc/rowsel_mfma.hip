@@ -92,7 +92,8 @@ __device__ __forceinline__ void limb_fragments(const uint32_t w[16], v4i f[4]) {
 // Limb packing: a p-major operand -> MFMA fragments.
 // Source word (row, k, p) at src[row * s_row + k * s_k + p] for rows
 // row_base .. rows-1 and k < K; fragment lane (li, lg) of (p, t, s, j) at
-// dst[p * d_p + t * d_t + s * d_s + (4 j + lg) * lpg + li] for li < lpg,
+// dst[p * d_p + (t / tgroup) * d_g + (t % tgroup) * d_t + s * d_s +
+// (4 j + lg) * lpg + li] for li < lpg,
 // holding limb j of row row_base + 16t + li at k = 64s + 16lg + 0..15 (with
 // lpg = 16 that is j * 64 + lane, whole 1 KiB fragments).  Rows past `rows`
 // and k past K give zero bytes.
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void pack_limbs4_kernel(PackDesc d, uint6
                               0x80808080u, 0x80808080u - q);  // x = 0 gives digit bytes 0
       v4i f[4];
       limb_fragments(w, f);
-      v4i* dst = static_cast<v4i*>(d.dst) + p * d.d_p + t * d.d_t + s * d.d_s + lg * d.lpg + li;
+      v4i* dst = static_cast<v4i*>(d.dst) + p * d.d_p + (t / d.tgroup) * d.d_g + (t % d.tgroup) * d.d_t +
+                 s * d.d_s + lg * d.lpg + li;
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[j * 4 * d.lpg] = f[j];
     }
@@ -173,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void pack_limbs_kernel(PackDesc d, uint64
     }
     v4i f[4];
     limb_fragments(w, f);
-    v4i* dst = static_cast<v4i*>(d.dst) + p * d.d_p + t * d.d_t + s * d.d_s + lg * d.lpg + li;
+    v4i* dst = static_cast<v4i*>(d.dst) + p * d.d_p + (t / d.tgroup) * d.d_g + (t % d.tgroup) * d.d_t +
+               s * d.d_s + lg * d.lpg + li;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dst[j * 4 * d.lpg] = f[j];
   }
@@ -182,6 +185,21 @@ __global__ __launch_bounds__(kThreads) void pack_limbs_kernel(PackDesc d, uint64
 // ---------------------------------------------------------------------------
 // The scan.
 // ---------------------------------------------------------------------------
+
+// The packed DB keeps column tiles in groups whose fragments follow each
+// other step after step: per point [t / G][s][t % G][limb][lane], so the
+// tiles a workgroup scans form one contiguous run.  G = 16 (T padded to a
+// multiple of 16; measured best against 1, 4 and 8), or T itself below 16.
+__host__ __device__ __forceinline__ uint32_t tile_group(uint32_t T) { return T < 16 ? T : 16; }
+__host__ __device__ __forceinline__ uint32_t padded_tiles(uint32_t T) {
+  const uint32_t G = tile_group(T);
+  return (T + G - 1) / G * G;
+}
+// Offset (in 16-byte units) of fragment (point p, column tile t, step 0, limb 0).
+__device__ __forceinline__ uint64_t db_tile_offset(uint64_t p, uint32_t t, uint32_t S, uint32_t T) {
+  const uint32_t G = tile_group(T);
+  return (p * padded_tiles(T) + (uint64_t)(t / G) * G) * S * kFrag + (uint64_t)(t % G) * kFrag;
+}
 
 struct MfmaEpilogue {
   uint32_t w[kMaxLimbs][7];  // 2^(8d) mod q
@@ -259,11 +277,12 @@ void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict
   const uint32_t limb = (uint32_t)(p / a.N);
 
   // this wave's column tiles (clamped for dead waves and the last group)
+  const uint64_t gstride = (uint64_t)tile_group(T) * kFrag;  // one step of a tile group
   const v4i* bcol[NTW];
 #pragma unroll
   for (int b = 0; b < NTW; ++b) {
     const uint32_t t = g * NTW + b < T ? g * NTW + b : T - 1;
-    bcol[b] = dbp + ((p * T + t) * S) * kFrag + lane;
+    bcol[b] = dbp + db_tile_offset(p, t, S, T) + lane;
   }
   const v4i* ap = limbs + (p * S) * (uint64_t)(MT * kFrag) + lane;
 
@@ -281,7 +300,7 @@ void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict
 #pragma unroll
     for (int b = 0; b < NTW; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bb[slot][b][j] = __builtin_nontemporal_load(bcol[b] + ss * kFrag + j * 64);
+      for (int j = 0; j < 4; ++j) bb[slot][b][j] = __builtin_nontemporal_load(bcol[b] + ss * gstride + j * 64);
   };
   // step s's A fragments -> ring slot s % kRing; wave w moves fragments w, w+4
   auto issue_a = [&](uint32_t s) {
@@ -369,11 +388,12 @@ __global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLa
   const uint32_t mrows = a.m - m_base;  // 1..16: the compact A's lanes per k-group
   const uint32_t astep = 16 * mrows;    // A fragments of one step: 4 limbs x 4 groups x mrows
 
+  const uint64_t gstride = (uint64_t)tile_group(T) * kFrag;  // one step of a tile group
   const v4i* bcol[NTW];
 #pragma unroll
   for (int b = 0; b < NTW; ++b) {
     const uint32_t t = g * NTW + b < T ? g * NTW + b : T - 1;
-    bcol[b] = dbp + ((p * T + t) * S) * kFrag + lane;
+    bcol[b] = dbp + db_tile_offset(p, t, S, T) + lane;
   }
   const v4i* ap = limbs + p * S * astep + lg * mrows + (li < mrows ? li : 0);
 
@@ -390,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLa
 #pragma unroll
     for (int b = 0; b < NTW; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bb[slot][b][j] = __builtin_nontemporal_load(bcol[b] + ss * kFrag + j * 64);
+      for (int j = 0; j < 4; ++j) bb[slot][b][j] = __builtin_nontemporal_load(bcol[b] + ss * gstride + j * 64);
   };
   auto step = [&](auto slot_tag, uint32_t s) {
     constexpr int slot = decltype(slot_tag)::value;
@@ -471,7 +491,7 @@ bool rowsel_packed_ok(const uint32_t* q, uint32_t R, uint32_t D0) {
 }
 
 uint64_t packed_layout_bytes(uint64_t P, uint32_t D0, uint32_t D1) {
-  return P * tiles_of(D1) * steps_of(D0) * (uint64_t)kFrag * 16;
+  return P * padded_tiles(tiles_of(D1)) * steps_of(D0) * (uint64_t)kFrag * 16;
 }
 
 hipError_t launch_pack(const PackDesc& d, hipStream_t stream) {
@@ -506,9 +526,11 @@ hipError_t launch_pack_operand(const uint32_t* src, void* dst, uint64_t P, uint3
   d.tiles = tiles_of(rows);
   d.S = steps_of(K);
   d.lpg = 16;
-  d.d_s = kFrag;
-  d.d_t = (uint64_t)d.S * kFrag;
-  d.d_p = (uint64_t)d.tiles * d.d_t;
+  d.tgroup = tile_group(d.tiles);
+  d.d_t = kFrag;
+  d.d_s = (uint64_t)d.tgroup * kFrag;
+  d.d_g = (uint64_t)d.S * d.d_s;
+  d.d_p = (uint64_t)padded_tiles(d.tiles) * d.S * kFrag;
   for (uint32_t r = 0; r < R; ++r) d.q[r] = q[r];
   return launch_pack(d, stream);
 }
@@ -556,8 +578,10 @@ hipError_t launch_rowsel_packed(const RowselLaunch& a, uint32_t R, void* workspa
     d.tiles = direct ? 1 : 2;
     d.lpg = direct ? rows : 16;
     d.S = S;
+    d.tgroup = d.tiles;  // one group: [p][s][tile][limb][group][lane]
     d.d_t = 16ull * d.lpg;
     d.d_s = d.tiles * d.d_t;
+    d.d_g = 0;
     d.d_p = (uint64_t)S * d.d_s;
     for (uint32_t r = 0; r < R; ++r) d.q[r] = a.lc.q[r];
     if ((e = launch_pack(d, stream)) != hipSuccess) return e;

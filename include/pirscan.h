@@ -78,8 +78,9 @@ typedef struct {
 /* Bytes of the tiled RowSel database produced by pirscan_layout_db, or 0 if
  * the shape is invalid.  When every q[r] < 2^31 and D0 <= 16384 the database
  * is stored for the int8 matrix-core scan: per point, ceil(D1/16) column
- * tiles x ceil(D0/64) k-steps x 4 KiB (exactly 4 * P * D0 * D1 when 16 | D1
- * and 64 | D0).  Otherwise it is stored word for word for the 64-bit VALU
+ * tiles (rounded up to a multiple of 16 from 16 tiles on) x ceil(D0/64)
+ * k-steps x 4 KiB (exactly 4 * P * D0 * D1 when 256 | D1 and 64 | D0, or
+ * D1 = 16 * T with T < 16).  Otherwise it is stored word for word for the 64-bit VALU
  * scan: 4 * P * D0 * D1. */
 size_t pirscan_layout_db_bytes(const pirscan_rowsel_shape* s);
 

@@ -53,8 +53,11 @@ Q3 = [536813569, 536690689, 536641537]
 def test_layout_bytes_and_invalid_shapes():
     s = pirscan.RowselShape.make(4096, Q3, 1024, 1024)
     assert pirscan.layout_db_bytes(s) == 51539607552  # 48 GiB: the packed limbs are exactly the words
-    # packed (every q < 2^31, D0 <= 16384): per point ceil(D1/16) x ceil(D0/64) x 4 KiB fragments
+    # packed (every q < 2^31, D0 <= 16384): per point ceil(D1/16) column tiles
+    # (rounded up to a multiple of 16 from 16 tiles on) x ceil(D0/64) steps x 4 KiB
     assert pirscan.layout_db_bytes(pirscan.RowselShape.make(16, Q3, 65, 17)) == 48 * 2 * 2 * 4096
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(16, Q3, 65, 240)) == 48 * 15 * 2 * 4096
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(16, Q3, 65, 300)) == 48 * 32 * 2 * 4096
     assert pirscan.layout_db_bytes(pirscan.RowselShape.make(4, [7], 1, 1)) == 4 * 4096
     # word layout for the VALU scan: a modulus >= 2^31, or D0 > 16384
     assert pirscan.layout_db_bytes(pirscan.RowselShape.make(16, [2147483659], 65, 17)) == 4 * 16 * 65 * 17
