@@ -213,24 +213,28 @@ class Workloads:
                              res_b, 2 * res_b, NTT_COUNT, bfly, "ntt"),
         }
 
-    def shape_scans(self):
-        """The scalar product at the hint, second-fold and aspect-ratio shapes,
-        each on the leading M*K bytes of the 64 GiB database buffer."""
+    def shape_scans(self, M, K, names):
+        """The scalar product at the hint, second-fold and aspect-ratio shapes
+        that view the leading M*K bytes of the 64 GiB database as [M][K]: that
+        view is tiled once (as the step's DB is) and every listed shape scans
+        the tiled copy.  Returns (tiled buffer, {name: scan})."""
         torch, pz = self.torch, self.pirscan
         import synth
 
         dev = torch.device("cuda:0")
-        flat = self.sdb.view(-1)
+        db = self.sdb.view(-1)[:M * K].view(M, K)
+        tiled = torch.empty(pz.scalar_layout_db_bytes(M, K), dtype=torch.uint8, device=dev)
+        pz.scalar_layout_db(db, tiled)
         out = {}
-        for name, (M, K, B) in SHAPE_SCANS.items():
-            db = flat[:M * K].view(M, K)
+        for name in names:
+            B = SHAPE_SCANS[name][2]
             q = torch.empty((K, B), dtype=torch.int32, device=dev)
             synth.fill_uint32_(q, SEEDS["scalar"], synth.STREAM_SCALAR_Q)
             o = torch.empty((M, B), dtype=torch.int32, device=dev)
-            ws = torch.empty(pz.scalar_workspace_bytes(M, K, B), dtype=torch.uint8, device=dev)
-            out[name] = ((lambda db=db, q=q, o=o, ws=ws: pz.scalar_gemm_u32(db, q, o, ws)),
+            ws = torch.empty(pz.scalar_tiled_workspace_bytes(M, K, B), dtype=torch.uint8, device=dev)
+            out[name] = ((lambda q=q, o=o, ws=ws, M=M, K=K: pz.scalar_gemm_u32_tiled(tiled, M, K, q, o, ws)),
                          M * K, M * K + 4 * K * B + 4 * M * B, B, M * K * B, "scalar")
-        return out
+        return tiled, out
 
     # name -> (callable, DB bytes, algorithmic HBM bytes, queries, macs, kind)
     def scans(self):
@@ -329,7 +333,8 @@ SCAN_KERNELS = {
     "scalar_64GiB_B32": "mfma_kernel<8, true>",
     "exppack_15GiB_B1": "rowsel_packed_direct_kernel<1>",
     "exppack_15GiB_B16": "rowsel_packed_kernel<2, 2",
-    **{name: ("gemv_kernel" if B == 1 else "mfma_kernel<8, false>") for name, (M, K, B) in SHAPE_SCANS.items()},
+    **{name: ("gemv_tiled_kernel" if B == 1 else "mfma_kernel<8, true>" if B <= 32 else "mfma_kernel<16, true>")
+       for name, (M, K, B) in SHAPE_SCANS.items()},
     "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
     "ntt_inv_hint": "ntt_kernel<12, true>",
     "ntt_fwd_hint": "ntt_kernel<12, false>",
@@ -611,11 +616,19 @@ def main():
     shape_rows = None
     if not args.skip_shapes:
         log("next rows: scalar product at the hint, second-fold and D/D0 shapes")
-        sscans = w.shape_scans()
-        _, stimes = time_scans(torch, w.pirscan, sscans, nsteps, 1, stream)
-        shape_rows = {name: workload_entry(name, sscans[name], *stimes[name]) for name in sscans}
-        del sscans
+        del w.sdbt  # the step's tiled DB; each [M][K] view below is tiled in turn
         torch.cuda.empty_cache()
+        shape_rows = {}
+        views = {}
+        for name, (M, K, B) in SHAPE_SCANS.items():
+            views.setdefault((M, K), []).append(name)
+        for (M, K), names in views.items():
+            tiled, sscans = w.shape_scans(M, K, names)
+            _, stimes = time_scans(torch, w.pirscan, sscans, nsteps, 1, stream)
+            shape_rows.update({name: workload_entry(name, sscans[name], *stimes[name]) for name in sscans})
+            del tiled, sscans
+            torch.cuda.empty_cache()
+        shape_rows = {name: shape_rows[name] for name in SHAPE_SCANS}
 
     w.setup_ntt()
     log("next rows: NTT / INTT over the hint's polynomials")

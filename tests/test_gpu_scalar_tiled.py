@@ -127,3 +127,29 @@ def test_tiled_64gib_sampled():
         del d_q
     del t
     release()
+
+
+def test_tiled_hint_and_second_fold_sampled():
+    """VIPIR's offline hint (the 2^20 x 2^16 database view times the
+    2^16 x 1280 matrix A: 20 passes of 64 query columns) and the double-packing
+    second fold (32768 x 2^17 times 2^17 x 1281) on tiled copies of the 64 GiB
+    database's leading bytes, as the benchmark runs them."""
+    import torch
+
+    seed, N_LWE = 5, 1280
+    say("scalar tiled hint / second fold: synthesising 64 GiB")
+    d_bytes = torch.empty(1 << 36, dtype=torch.int8, device="cuda:0")
+    synth.fill_int8_(d_bytes, seed, synth.STREAM_SCALAR_DB)
+    for M, K, B, rows, qseed in (((1 << 20), (1 << 16), N_LWE, [0, 777, (1 << 20) - 1], seed + 100),
+                                 (32768, 1 << 17, N_LWE + 1, [0, 4097, 32767], seed + 200)):
+        say(f"  M={M} K={K} B={B}")
+        t = tiled(d_bytes[:M * K].view(M, K))
+        d_q = empty_u32((K, B))
+        synth.fill_uint32_(d_q, qseed, synth.STREAM_SCALAR_Q)
+        got = to_host_u32(scan(t, M, K, d_q).index_select(0, torch.tensor(rows, device="cuda:0")))
+        db_s = synth.int8_rows(seed, synth.STREAM_SCALAR_DB, K, rows)
+        np.testing.assert_array_equal(got, oracle.scalar(db_s, synth.uint32_array(qseed, synth.STREAM_SCALAR_Q, (K, B))))
+        del t, d_q
+        release()
+    del d_bytes
+    release()
