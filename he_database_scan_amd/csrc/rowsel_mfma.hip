@@ -49,6 +49,12 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kRing = 3;         // A-fragment ring depth in steps
+#ifndef PIRSCAN_SMALL_ROWS
+#define PIRSCAN_SMALL_ROWS 4
+#endif
+#ifndef PIRSCAN_SMALL_NTW
+#define PIRSCAN_SMALL_NTW 1
+#endif
 constexpr uint32_t kDirectRows = 16;  // passes of at most this many rows: the direct kernel
 constexpr uint32_t kFrag = 256;  // v4i per step and 16-row (or 16-column) tile: 4 limbs x 64 lanes
 
@@ -588,7 +594,7 @@ hipError_t launch_rowsel_packed(const RowselLaunch& a, uint32_t R, void* workspa
     timer_mark_start(stream);  // first pass only
     // one column tile per wave while the A stream is small next to the DB's
     // (rows <= 4: at most a quarter), four beyond, which divides it by four
-    if (direct && rows <= 4) e = launch_scan_direct<1>(a, ep, limbs, dbp, out_t, m_base, stream);
+    if (direct && rows <= PIRSCAN_SMALL_ROWS) e = launch_scan_direct<PIRSCAN_SMALL_NTW>(a, ep, limbs, dbp, out_t, m_base, stream);
     else if (direct) e = launch_scan_direct<4>(a, ep, limbs, dbp, out_t, m_base, stream);
     else e = launch_scan<2, 2>(a, ep, limbs, dbp, out_t, m_base, stream);
     if (e != hipSuccess) return e;
