@@ -55,6 +55,9 @@ constexpr int kRing = 3;         // A-fragment ring depth in steps
 #ifndef PIRSCAN_SMALL_NTW
 #define PIRSCAN_SMALL_NTW 1
 #endif
+#ifndef PIRSCAN_DIRECT_DEPTH
+#define PIRSCAN_DIRECT_DEPTH 3  // steps in the one-tile direct kernel's register ring (2 or 3)
+#endif
 constexpr uint32_t kDirectRows = 16;  // passes of at most this many rows: the direct kernel
 constexpr uint32_t kFrag = 256;  // v4i per step and 16-row (or 16-column) tile: 4 limbs x 64 lanes
 
@@ -215,11 +218,31 @@ struct MfmaEpilogue {
 #ifndef PIRSCAN_NT_STORE
 #define PIRSCAN_NT_STORE 1
 #endif
+#ifndef PIRSCAN_STAGE_STORE
+#define PIRSCAN_STAGE_STORE 1  // outputs leave through LDS as whole-row 16-byte stores
+#endif
+
+// Residue of accumulator element e of (row tile mt, column tile b): the
+// seven diagonals folded with hi * (2^32 mod q) + lo, then one Barrett step.
+template <int MT, int NTW>
+__device__ __forceinline__ uint32_t fold_residue(const MfmaEpilogue& ep, const v4i (&acc)[7][MT][NTW], int mt,
+                                                 int b, int e, uint32_t limb, uint64_t c32, uint64_t mu,
+                                                 uint32_t q) {
+  uint64_t x = ep.corr[limb];
+#pragma unroll
+  for (int dd = 0; dd < 7; ++dd) {
+    x = (x >> 32) * c32 + (uint32_t)x;  // <= (2^32-1)(c32+1) < 2^63
+    x += (uint64_t)((uint32_t)acc[dd][mt][b][e] + 0x80000000u) * ep.w[limb][dd];
+  }
+  uint64_t r = x - __umul64hi(x, mu) * q;
+  if (r >= q) r -= q;
+  return (uint32_t)r;
+}
 
 // Epilogue of a wave: folds the seven diagonals of each accumulator element
 // into its residue and stores rows < m - m_base, columns < D1 of the wave's
-// tiles into out_t [P][m][D1].  D element e of lane (li, lg) is row
-// 4*lg + e, column li of the 16 x 16 tile.
+// tiles to out_t[p][m][D1]; lane (li, lg) holds rows mt * 16 + 4 * lg + e,
+// column li of the 16 x 16 tile.
 template <int MT, int NTW>
 __device__ __forceinline__ void store_outputs(const RowselLaunch& a, const MfmaEpilogue& ep,
                                               const v4i (&acc)[7][MT][NTW], uint32_t* __restrict__ out_t,
@@ -238,18 +261,54 @@ __device__ __forceinline__ void store_outputs(const RowselLaunch& a, const MfmaE
       for (int b = 0; b < NTW; ++b) {
         const uint32_t c = (g * NTW + b) * 16 + li;
         if (c >= a.D1) continue;
-        uint64_t x = ep.corr[limb];
-#pragma unroll
-        for (int dd = 0; dd < 7; ++dd) {
-          x = (x >> 32) * c32 + (uint32_t)x;  // <= (2^32-1)(c32+1) < 2^63
-          x += (uint64_t)((uint32_t)acc[dd][mt][b][e] + 0x80000000u) * ep.w[limb][dd];
-        }
-        uint64_t r = x - __umul64hi(x, mu) * q;
-        if (r >= q) r -= q;
+        const uint32_t r = fold_residue<MT, NTW>(ep, acc, mt, b, e, limb, c32, mu, q);
         uint32_t* dst = out_t + ((uint64_t)p * a.m + m_base + row) * a.D1 + c;
-        if (PIRSCAN_NT_STORE) __builtin_nontemporal_store((uint32_t)r, dst);
-        else *dst = (uint32_t)r;
+        if (PIRSCAN_NT_STORE) __builtin_nontemporal_store(r, dst);
+        else *dst = r;
       }
+    }
+  }
+}
+
+// The same residues written to an LDS block stage[row][col0 + b * 16 + li]
+// (row stride ld words), for a later store of whole rows.
+template <int MT, int NTW>
+__device__ __forceinline__ void stage_outputs(const RowselLaunch& a, const MfmaEpilogue& ep,
+                                              const v4i (&acc)[7][MT][NTW], uint32_t* stage, uint32_t ld,
+                                              uint32_t col0, uint32_t limb, uint32_t mrows, uint32_t lg,
+                                              uint32_t li) {
+  const uint64_t c32 = a.lc.c[limb], mu = a.lc.mu[limb];
+  const uint32_t q = a.lc.q[limb];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t row = mt * 16 + 4 * lg + e;
+      if (row >= mrows) continue;
+#pragma unroll
+      for (int b = 0; b < NTW; ++b)
+        stage[row * ld + col0 + b * 16 + li] = fold_residue<MT, NTW>(ep, acc, mt, b, e, limb, c32, mu, q);
+    }
+  }
+}
+
+// Rows 0 .. mrows-1 of an LDS block of `width` columns (a multiple of 4, row
+// stride ld, a multiple of 4) to out_t[p][m_base + row][c0 ..]: `threads`
+// consecutive threads (thread index `tid`) cover the block as 16-byte
+// stores, width / 4 per row, so each store instruction writes whole rows.
+// Needs D1 % 4 == 0 and c0 % 4 == 0 (16-byte aligned rows).
+__device__ __forceinline__ void store_staged(const uint32_t* stage, uint32_t ld, uint32_t width, uint32_t mrows,
+                                             uint32_t* __restrict__ out_t, uint64_t p, uint32_t m,
+                                             uint32_t m_base, uint32_t D1, uint32_t c0, uint32_t tid,
+                                             uint32_t threads) {
+  const uint32_t lpr = width / 4, rpp = threads / lpr;
+  for (uint32_t r0 = 0; r0 < mrows; r0 += rpp) {
+    const uint32_t row = r0 + tid / lpr, c4 = (tid % lpr) * 4;
+    if (row < mrows && tid < rpp * lpr && c0 + c4 < D1) {
+      const v4i v = *reinterpret_cast<const v4i*>(stage + row * ld + c4);
+      v4i* dst = reinterpret_cast<v4i*>(out_t + ((uint64_t)p * m + m_base + row) * D1 + c0 + c4);
+      if (PIRSCAN_NT_STORE) __builtin_nontemporal_store(v, dst);
+      else *dst = v;
     }
   }
 }
@@ -273,6 +332,8 @@ void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict
                           uint32_t S, uint32_t T, uint32_t ngroups, uint32_t gq) {
   constexpr int kAFrags = MT * 4;  // A fragments per step (row tile x limb)
   __shared__ v4i aring[kRing][kAFrags * 64];
+  constexpr uint32_t kStageLd = NTW * 16 + 4;  // a wave's output block: MT * 16 rows x NTW * 16 columns
+  __shared__ uint32_t ostage[PIRSCAN_STAGE_STORE ? 4 : 1][PIRSCAN_STAGE_STORE ? MT * 16 * kStageLd : 1];
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane % 16, lg = lane / 16;
@@ -366,6 +427,17 @@ void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict
   __builtin_amdgcn_s_waitcnt(0);  // no ring load may outlive the workgroup's LDS
 
   if (!live) return;
+  if (PIRSCAN_STAGE_STORE && a.D1 % 4 == 0) {
+    // through a wave-private LDS block, so each store writes whole 128-byte rows
+    uint32_t* st = ostage[PIRSCAN_STAGE_STORE ? wave : 0];
+    stage_outputs<MT, NTW>(a, ep, acc, st, kStageLd, 0, limb, a.m - m_base, lg, li);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    store_staged(st, kStageLd, NTW * 16, a.m - m_base < MT * 16 ? a.m - m_base : MT * 16, out_t, p, a.m, m_base,
+                 a.D1, g * NTW * 16, lane, 64);
+    return;
+  }
   store_outputs<MT, NTW>(a, ep, acc, out_t, p, g, limb, m_base, lg, li);
 }
 
@@ -383,11 +455,15 @@ __global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLa
                                                                         uint32_t* __restrict__ out_t,
                                                                         uint32_t m_base, uint32_t S, uint32_t T,
                                                                         uint32_t ngroups, uint64_t items) {
+  constexpr uint32_t kStageLd = 64 * NTW + 4;  // the workgroup's output block: up to 16 rows x 64 NTW columns
+  __shared__ uint32_t dstage[PIRSCAN_STAGE_STORE ? 16 * kStageLd : 1];
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane % 16, lg = lane / 16;
   const uint64_t item = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
-  if (item >= items) return;  // no barriers in this kernel
+  // a workgroup returns here whole or not at all whenever the staged store
+  // below (the kernel's only barrier) is taken: then items % 4 == 0
+  if (item >= items) return;
   const uint64_t p = item / ngroups;
   const uint32_t g = (uint32_t)(item % ngroups);
   const uint32_t limb = (uint32_t)(p / a.N);
@@ -408,7 +484,9 @@ __global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLa
   for (int dd = 0; dd < 7; ++dd)
 #pragma unroll
     for (int b = 0; b < NTW; ++b) acc[dd][0][b] = v4i{0, 0, 0, 0};
-  v4i aa[2][4], bb[2][NTW][4];
+  // a register ring of kDepth steps: step s + kDepth - 1 is loaded while s is multiplied
+  constexpr int kDepth = NTW == 1 ? PIRSCAN_DIRECT_DEPTH : 2;
+  v4i aa[kDepth][4], bb[kDepth][NTW][4];
   auto load = [&](int slot, uint32_t s) {
     const uint32_t ss = s < S ? s : S - 1;  // past the end: a harmless reload of the last step
 #pragma unroll
@@ -420,8 +498,8 @@ __global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLa
   };
   auto step = [&](auto slot_tag, uint32_t s) {
     constexpr int slot = decltype(slot_tag)::value;
-    load(slot ^ 1, s + 1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the next step's loads ahead of this step's MFMAs
+    load((slot + kDepth - 1) % kDepth, s + kDepth - 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the later steps' loads ahead of this step's MFMAs
 #pragma unroll
     for (int b = 0; b < NTW; ++b)
 #pragma unroll
@@ -431,13 +509,39 @@ __global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLa
           acc[i + j][0][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[slot][i], bb[slot][b][j], acc[i + j][0][b], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  load(0, 0);
-  uint32_t s = 0;
-  for (; s + 1 < S; s += 2) {
-    step(std::integral_constant<int, 0>{}, s);
-    step(std::integral_constant<int, 1>{}, s + 1);
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  using Slot2 = std::integral_constant<int, 2>;
+  if constexpr (kDepth == 2) {
+    load(0, 0);
+    uint32_t s = 0;
+    for (; s + 1 < S; s += 2) {
+      step(Slot0{}, s);
+      step(Slot1{}, s + 1);
+    }
+    if (s < S) step(Slot0{}, s);
+  } else {
+    static_assert(kDepth == 3, "the direct kernel's ring holds 2 or 3 steps");
+    load(0, 0);
+    load(1, 1);
+    uint32_t s = 0;
+    for (; s + 2 < S; s += 3) {
+      step(Slot0{}, s);
+      step(Slot1{}, s + 1);
+      step(Slot2{}, s + 2);
+    }
+    if (s < S) step(Slot0{}, s);
+    if (s + 1 < S) step(Slot1{}, s + 1);
   }
-  if (s < S) step(std::integral_constant<int, 0>{}, s);
+  if (PIRSCAN_STAGE_STORE && ngroups % 4 == 0 && a.D1 % 4 == 0) {
+    // every wave of the workgroup is live and on point p, tiles g - wave ..
+    // g - wave + 3: their rows meet in LDS and leave as whole-row stores
+    stage_outputs<1, NTW>(a, ep, acc, dstage, kStageLd, wave * NTW * 16, limb, mrows, lg, li);
+    __syncthreads();
+    store_staged(dstage, kStageLd, 64 * NTW, mrows, out_t, p, a.m, m_base, a.D1, (g - wave) * NTW * 16,
+                 threadIdx.x, kThreads);
+    return;
+  }
   store_outputs<1, NTW>(a, ep, acc, out_t, p, g, limb, m_base, lg, li);
 }
 
