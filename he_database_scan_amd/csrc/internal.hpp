@@ -177,6 +177,12 @@ hipError_t launch_ntt(const NttDesc& d, NttMode mode, const void* plan, const ui
 void timer_mark_start(hipStream_t stream);
 void timer_mark_stop(hipStream_t stream);
 
+// s_waitcnt immediate: vmcnt = n (< 64), expcnt and lgkmcnt left unconstrained.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// An LDS address for the direct global-to-LDS loads.
+#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(x))
+
 // Maps a hardware workgroup id to a logical tile id so that consecutive
 // logical tiles run on the same XCD (gfx950 dispatches workgroups round-robin
 // over its 8 XCDs, each with a private L2).

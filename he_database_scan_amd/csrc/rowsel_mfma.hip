@@ -313,10 +313,6 @@ __device__ __forceinline__ void store_staged(const uint32_t* stage, uint32_t ld,
   }
 }
 
-// s_waitcnt immediate: vmcnt = n (< 64), expcnt and lgkmcnt left unconstrained.
-constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(x))
 
 // Workgroup = 4 wavefronts on one point p; wave w scans column tiles
 // (4g' + w) * NTW .. + NTW-1 (g' = the workgroup's quad of tile groups) over

@@ -239,6 +239,11 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const uint32_t* __
 #ifndef PIRSCAN_SCALAR_MFMA_ROWTILES
 #define PIRSCAN_SCALAR_MFMA_ROWTILES 2
 #endif
+#ifndef PIRSCAN_SCALAR_BAHEAD
+#define PIRSCAN_SCALAR_BAHEAD 4  // digit fragments read ahead of their MFMAs (0: as the compiler schedules)
+#endif
+constexpr int kBAhead = PIRSCAN_SCALAR_BAHEAD;
+
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaRowTiles2 = PIRSCAN_SCALAR_MFMA_ROWTILES;  // 16-row tiles per wavefront
 constexpr int kMfmaDepth = PIRSCAN_SCALAR_MFMA_DEPTH;        // A ring depth in 64-k steps
@@ -360,16 +365,31 @@ __device__ __forceinline__ void mfma_tile(const int8_t* __restrict__ db, const u
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         const v4i* bl = reinterpret_cast<const v4i*>(bsm[cc & 1]);
+        // digit fragment i = s * NT + ct of the chunk; with kBAhead > 0 the
+        // fragments are read kBAhead ahead of their MFMAs, through the chunk
+        constexpr int kNB = kMfmaChunkSteps * NT;
+        constexpr int kBA = kBAhead < kNB ? kBAhead : kNB;
+        auto bfrag = [&](int i) -> v4i { return bl[((i / NT) * 4 + lg) * DCOLS + (i % NT) * 16 + li]; };
+        v4i bq[kBA > 0 ? kBA : 1];
+#pragma unroll
+        for (int i = 0; i < kBA; ++i) bq[i] = bfrag(i);
 #pragma unroll
         for (int s = 0; s < kMfmaChunkSteps; ++s) {
           const uint32_t step = cc * kMfmaChunkSteps + s;
           const int slot = (half * kMfmaChunkSteps + s) % DEPTH;
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
-            const v4i bf = bl[(s * 4 + lg) * DCOLS + ct * 16 + li];
+            const int i = s * NT + ct;
+            const v4i bf = kBA > 0 ? bq[i % (kBA > 0 ? kBA : 1)] : bfrag(i);
 #pragma unroll
             for (int rt = 0; rt < kMfmaRowTiles2; ++rt)
               acc[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[slot][rt], bf, acc[rt][ct], 0, 0, 0);
+            if (kBA > 0 && i + kBA < kNB) {
+              bq[i % (kBA > 0 ? kBA : 1)] = bfrag(i + kBA);
+              // pin the read here, kBA fragments ahead of its MFMAs: left
+              // alone the scheduler sinks it next to its use
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
           if (s & 1) {
             // Refill the slots of steps s-1 and s together: the two 64-byte
