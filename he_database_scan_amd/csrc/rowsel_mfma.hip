@@ -320,7 +320,8 @@ __device__ __forceinline__ void store_staged(const uint32_t* stage, uint32_t ld,
 // consumes NTW x 4 KiB of packed DB from HBM (register double buffer, one
 // step ahead) and MT x 4 KiB of A fragments from the shared LDS ring, and
 // issues 16 * MT * NTW MFMAs.  Waves past the last tile group run the same
-// loads, barriers and MFMAs on clamped tiles and store nothing.
+// loads, barriers and MFMAs on clamped tiles and store nothing.  Each live
+// wave's residues leave through its own LDS block as whole 128-byte rows.
 template <int MT, int NTW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2 : 3)))
 void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict__ limbs,
@@ -437,9 +438,10 @@ void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict
   store_outputs<MT, NTW>(a, ep, acc, out_t, p, g, limb, m_base, lg, li);
 }
 
-// Small batches (one pass of at most 16 rows): no LDS ring and no barriers.
-// Each wave (point p, column tiles g*NTW .. g*NTW+NTW-1) loads its own A
-// fragments one step ahead with the DB fragments.  The A side is packed
+// Small batches (one pass of at most 16 rows): no LDS ring, and a barrier
+// only in the epilogue.  Each wave (point p, column tiles g*NTW ..
+// g*NTW+NTW-1) loads its own A fragments with the DB fragments, kDepth - 1
+// steps ahead (a register ring).  The A side is packed
 // compactly, lanes_per_group = mrows (only the live rows of each k-group), so
 // it costs the bytes of ct itself; lanes of rows past mrows read their group's
 // row-0 lane instead (same line, no branch).  Their output rows are copies of
