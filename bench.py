@@ -110,7 +110,10 @@ def code_text(text: str) -> str:
 
 
 def source_hash(path: str) -> str:
-    return hashlib.sha256(code_text(open(path).read()).encode()).hexdigest()[:16]
+    """The kernel file's code together with the shared header it includes."""
+    header = os.path.join(os.path.dirname(path), "internal.hpp")
+    text = code_text(open(path).read()) + "\n" + code_text(open(header).read())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def log(msg: str) -> None:
