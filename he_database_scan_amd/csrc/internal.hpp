@@ -193,4 +193,23 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t pid, uint32_t num) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Logical workgroup id of hardware id h (gfx950 deals workgroups to its 8
+// XCDs round-robin).  C > 1: XCD x takes the C-id chunks x, x + 8, x + 16,
+// ... so the eight XCDs stream neighbouring parts of a database at any time
+// (ids past the last whole round of 8 chunks keep their hardware order); 1:
+// no remap; 0: xcd_remap, each XCD one contiguous eighth of the grid.
+template <uint32_t C>
+__device__ __forceinline__ uint32_t scan_remap(uint32_t h, uint32_t num) {
+  if constexpr (C == 0) {
+    return xcd_remap(h, num);
+  } else if constexpr (C == 1) {
+    return h;
+  } else {
+    const uint32_t full = num / (8 * C) * (8 * C);
+    if (h >= full) return h;
+    const uint32_t x = h % 8, l = h / 8;
+    return ((l / C) * 8 + x) * C + l % C;
+  }
+}
+
 }  // namespace pirscan

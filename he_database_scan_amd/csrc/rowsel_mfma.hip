@@ -195,6 +195,15 @@ __global__ __launch_bounds__(kThreads) void pack_limbs_kernel(PackDesc d, uint64
 // The scan.
 // ---------------------------------------------------------------------------
 
+#ifndef PIRSCAN_DIRECT_XCD_CHUNK
+#define PIRSCAN_DIRECT_XCD_CHUNK 64  // workgroups per XCD chunk, up-to-16-row scan (4 points)
+#endif
+#ifndef PIRSCAN_RING_XCD_CHUNK
+#define PIRSCAN_RING_XCD_CHUNK 8  // workgroups per XCD chunk, 17-32-row scan (1 point at D1 = 1024)
+#endif
+// (scan_remap: measured at 48 GiB, one contiguous eighth of the grid per XCD
+// is 7-9% slower than chunks of 8-64 workgroups dealt round the XCDs, at
+// every batch size.)
 // The packed DB keeps column tiles in groups whose fragments follow each
 // other step after step: per point [t / G][s][t % G][limb][lane], so the
 // tiles a workgroup scans form one contiguous run.  G = 16 (T padded to a
@@ -334,7 +343,7 @@ void rowsel_packed_kernel(RowselLaunch a, MfmaEpilogue ep, const v4i* __restrict
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane % 16, lg = lane / 16;
-  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);  // grid = P * gq exactly
+  const uint32_t wg = scan_remap<PIRSCAN_RING_XCD_CHUNK>(blockIdx.x, gridDim.x);  // grid = P * gq exactly
   const uint64_t p = wg / gq;
   const uint32_t g = (wg % gq) * 4 + wave;
   const bool live = g < ngroups;
@@ -458,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void rowsel_packed_direct_kernel(RowselLa
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane % 16, lg = lane / 16;
-  const uint64_t item = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
+  const uint64_t item = (uint64_t)scan_remap<PIRSCAN_DIRECT_XCD_CHUNK>(blockIdx.x, gridDim.x) * 4 + wave;
   // a workgroup returns here whole or not at all whenever the staged store
   // below (the kernel's only barrier) is taken: then items % 4 == 0
   if (item >= items) return;
