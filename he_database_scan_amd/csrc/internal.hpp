@@ -186,7 +186,7 @@ constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 
 // Maps a hardware workgroup id to a logical tile id so that consecutive
 // logical tiles run on the same XCD (gfx950 dispatches workgroups round-robin
 // over its 8 XCDs, each with a private L2).
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t pid, uint32_t num) {
+__host__ __device__ __forceinline__ uint32_t xcd_remap(uint32_t pid, uint32_t num) {
   constexpr uint32_t kXcds = 8;
   const uint32_t xcd = pid % kXcds, local = pid / kXcds;
   const uint32_t per = num / kXcds, rem = num % kXcds;
@@ -199,7 +199,7 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t pid, uint32_t num) {
 // (ids past the last whole round of 8 chunks keep their hardware order); 1:
 // no remap; 0: xcd_remap, each XCD one contiguous eighth of the grid.
 template <uint32_t C>
-__device__ __forceinline__ uint32_t scan_remap(uint32_t h, uint32_t num) {
+__host__ __device__ __forceinline__ uint32_t scan_remap(uint32_t h, uint32_t num) {
   if constexpr (C == 0) {
     return xcd_remap(h, num);
   } else if constexpr (C == 1) {
