@@ -228,6 +228,33 @@ def test_every_batch_size_on_one_layout():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("D1", [256, 512])
+def test_whole_row_stores_on_whole_groups(D1):
+    """Column counts that split into whole groups of four workgroup waves
+    (D1 = 256: 16 column tiles; 512: 32) take the epilogue that gathers the
+    residues in LDS and stores whole rows: every batch-size class (1-4 rows
+    with one tile per wave, 5-16 with four, 17-32 on the shared ring, and a
+    second pass), with a ragged k extent and enough points for several
+    workgroup chunks per XCD."""
+    import torch
+
+    N, q, D0 = 64, MED_Q, 130
+    P = N * len(q)
+    rng = np.random.default_rng(D1 + 5)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    shape = pirscan.RowselShape.make(N, q, D0, D1)
+    d_dbt = empty_bytes(pirscan.layout_db_bytes(shape))
+    pirscan.layout_db(shape, to_dev_u32(db), d_dbt)
+    for m in (1, 2, 4, 5, 8, 13, 16, 17, 24, 32, 33, 48):
+        say(f"rowsel whole-row stores D1={D1} m={m}")
+        ct = rand_res(rng, (m, D0, P), N, q)
+        d_out = empty_u32((m, D1, P))
+        pirscan.rowsel_modgemm(shape, m, to_dev_u32(ct), d_dbt, d_out, workspace(shape, m))
+        np.testing.assert_array_equal(to_host_u32(d_out), oracle.rowsel(ct, db, N, q))
+        del d_out
+    torch.cuda.synchronize()
+
+
 def signed_limb_value(digits):
     return sum(int(d) << (8 * i) for i, d in enumerate(digits))
 
