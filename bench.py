@@ -512,6 +512,23 @@ def cpu_baseline(budget_s: float = 4.0):
     return rates, threads, "; ".join(samples)
 
 
+def read_reference(torch, pirscan, bufs, steps, warmup, stream):
+    """The library's read-stream reference (one non-temporal 16-byte read pass,
+    no arithmetic) over each tiled database, timed like the scans: the HBM
+    rate a plain read of the same buffer reaches on this device and run."""
+    sink = torch.empty(256, dtype=torch.uint8, device="cuda:0")
+    scans = {name: ((lambda b=b: pirscan.bench_read(b, sink)), b.numel() * b.element_size())
+             for name, b in bufs.items()}
+    _, times = time_scans(torch, pirscan, scans, steps, warmup, stream)
+    out = {}
+    for name, (call_ms, kern_ms) in times.items():
+        nbytes = scans[name][1]
+        k = sorted(kern_ms)[len(kern_ms) // 2]
+        out[name] = {"bytes": nbytes, "kernel_ms": k, "kernel_ms_min": min(kern_ms),
+                     "GBps": nbytes / (k * 1e-3) / 1e9, "frac": nbytes / (k * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def time_scans(torch, pirscan, scans, steps, warmup, stream):
     """Runs `warmup` untimed rounds of the scans, then times `steps` rounds:
     HIP events around each scan call and, through the library's kernel timer,
@@ -619,6 +636,10 @@ def main():
     value = total_db * args.steps / wall / 1e9
     dominant = max(per, key=lambda k: per[k]["kernel_ms"])
 
+    log("read reference: one plain read pass over each tiled database")
+    read_ref = read_reference(torch, w.pirscan, {"rowsel_48GiB_db": w.dbt, "scalar_64GiB_db": w.sdbt},
+                              args.steps, min(args.warmup, 1), stream)
+
     log("next rows: ExpPack packing GEMM")
     nscans = w.next_scans()
     _, ntimes = time_scans(torch, w.pirscan, nscans, args.steps, args.warmup, stream)
@@ -668,6 +689,7 @@ def main():
                    "hbm_frac_of_step": value / HBM_PEAK_GBS,
                    "layout_db_once_ms": w.layout_s * 1e3, "scalar_layout_db_once_ms": w.slayout_s * 1e3},
         "roofline": dict(per[dominant]["roofline"], kernel=SCAN_KERNELS[dominant], scan=dominant),
+        "hbm_read_reference": read_ref,
         "workloads": per,
         "next_rows": {"exppack": {"config": {"N": RS_N, "R": len(RS_Q), "Dr": EP_DR, "n": EP_N, "B": [1, 16],
                                              "hint_GiB": 4 * RS_N * len(RS_Q) * EP_DR * EP_N / 2**30},

@@ -177,6 +177,10 @@ hipError_t launch_ntt(const NttDesc& d, NttMode mode, const void* plan, const ui
 void timer_mark_start(hipStream_t stream);
 void timer_mark_stop(hipStream_t stream);
 
+// Benchmark reference: one non-temporal 16-byte read pass over `bytes` of buf
+// (bytes % 16 == 0, buf 16-byte aligned), timed by the kernel-timer hook.
+hipError_t launch_read_stream(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // s_waitcnt immediate: vmcnt = n (< 64), expcnt and lgkmcnt left unconstrained.
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 

@@ -567,6 +567,14 @@ int pirscan_kernel_timer_end(float* ms, uint32_t max_count, uint32_t* count) {
   return st;
 }
 
+int pirscan_bench_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0) return PIRSCAN_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0) return PIRSCAN_EINVAL;
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  return device_status(pirscan::launch_read_stream(buf, bytes, sink, (hipStream_t)stream));
+}
+
 const char* pirscan_strerror(int status) {
   switch (status) {
     case PIRSCAN_OK: return "ok";

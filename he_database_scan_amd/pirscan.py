@@ -163,6 +163,8 @@ def _load():
         L.pirscan_kernel_timer_begin.restype = ctypes.c_int
         L.pirscan_kernel_timer_end.argtypes = [ctypes.POINTER(ctypes.c_float), u32, ctypes.POINTER(u32)]
         L.pirscan_kernel_timer_end.restype = ctypes.c_int
+        L.pirscan_bench_read.argtypes = [vp, sz, vp, vp]
+        L.pirscan_bench_read.restype = ctypes.c_int
         L.pirscan_strerror.argtypes = [ctypes.c_int]
         L.pirscan_strerror.restype = ctypes.c_char_p
         L.pirscan_version.argtypes = []
@@ -393,6 +395,17 @@ def ntt_rns_forward(shape: NttShape, plan, coeffs, out, stream=None) -> None:
     """out[c][r][:] = NTT of (coeffs[c][:] mod q[r]): coeffs [count][N] integers
     in [0, 2^32) as uint32 bits, out [count][R][N]."""
     _ntt_call("pirscan_ntt_rns_forward", shape, plan, coeffs, out, shape.N, stream)
+
+
+def bench_read(buf, sink, stream=None) -> None:
+    """Benchmark reference: one non-temporal read pass over the device buffer
+    ``buf`` (16-byte aligned, a multiple of 16 bytes); ``sink`` is a device
+    buffer of at least 4 bytes whose contents become unspecified."""
+    nbytes = buf.numel() * buf.element_size()
+    _dev_bytes(sink, "sink", 4)
+    if buf.device.type != "cuda":
+        raise ValueError("buf must be a device tensor")
+    _check("pirscan_bench_read", _load().pirscan_bench_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
 
 
 def kernel_timer_begin(capacity: int) -> None:

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PIRSCAN_VERSION 10300 /* 1.3.0 */
+#define PIRSCAN_VERSION 10400 /* 1.4.0 */
 #define PIRSCAN_MAX_R 8
 
 enum {
@@ -335,6 +335,19 @@ int pirscan_ntt_rns_forward(const pirscan_ntt_shape* s, const void* plan, const 
  */
 int pirscan_kernel_timer_begin(uint32_t capacity);
 int pirscan_kernel_timer_end(float* ms, uint32_t max_count, uint32_t* count);
+
+/*
+ * Benchmark reference (not part of the scan): one pass of 16-byte
+ * non-temporal loads over `bytes` of the device buffer buf -- the access the
+ * scans make to their databases, without their arithmetic -- so that a
+ * scan's HBM rate can be compared with a plain read stream's on the same
+ * device.  Timed by the kernel-timer hook like a scan call.  buf: device
+ * memory, 16-byte aligned, bytes a non-zero multiple of 16, only read.
+ * sink: device memory of at least 4 bytes that a thread may overwrite with
+ * its running xor (which keeps the loads from being optimised away); its
+ * contents are unspecified afterwards.  PIRSCAN_EINVAL otherwise.
+ */
+int pirscan_bench_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* pirscan_strerror(int status);

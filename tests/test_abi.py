@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
                  "pirscan_exppack_workspace_bytes", "pirscan_exppack_modgemm",
                  "pirscan_ntt_plan_bytes", "pirscan_ntt_plan_init", "pirscan_ntt_forward",
                  "pirscan_ntt_inverse", "pirscan_ntt_rns_forward",
-                 "pirscan_kernel_timer_begin", "pirscan_kernel_timer_end",
+                 "pirscan_kernel_timer_begin", "pirscan_kernel_timer_end", "pirscan_bench_read",
                  "pirscan_version", "pirscan_last_device_error"):
         assert want in names
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert pirscan.version() == 10300
+    assert pirscan.version() == 10400
     assert pirscan.strerror(0) == "ok"
     assert "invalid" in pirscan.strerror(-1)
     assert "gfx950" in pirscan.strerror(-3)
@@ -263,6 +263,18 @@ def test_kernel_timer_argument_checks():
     assert L.pirscan_kernel_timer_begin((1 << 20) + 1) == pirscan.EINVAL
     n = ctypes.c_uint32(7)
     assert L.pirscan_kernel_timer_end(None, 0, ctypes.byref(n)) == pirscan.EINVAL   # not begun
+
+
+def test_bench_read_argument_checks():
+    """The read-stream reference validates before touching a device."""
+    L = pirscan.lib()
+    vp = ctypes.c_void_p
+    buf, sink = vp(1 << 20), vp(1 << 21)   # never dereferenced: every call below is rejected first
+    assert L.pirscan_bench_read(None, 4096, sink, None) == pirscan.EINVAL
+    assert L.pirscan_bench_read(buf, 4096, None, None) == pirscan.EINVAL
+    assert L.pirscan_bench_read(buf, 0, sink, None) == pirscan.EINVAL
+    assert L.pirscan_bench_read(buf, 4100, sink, None) == pirscan.EINVAL
+    assert L.pirscan_bench_read(vp((1 << 20) + 4), 4096, sink, None) == pirscan.EINVAL
 
 
 # primitive 2N-th roots of unity (N = 4096) for the three 29-bit primes: each

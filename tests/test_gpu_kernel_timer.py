@@ -57,3 +57,25 @@ def test_one_time_per_call_within_the_call():
     calls[0]()
     with pytest.raises(pirscan.PirscanError):
         pirscan.kernel_timer_end(4)
+
+
+def test_read_reference_is_timed_and_reads_only():
+    """The read-stream reference runs on any multiple of 16 bytes (whole
+    unrolled rounds and a tail), records one kernel time per call, and leaves
+    the buffer it reads untouched."""
+    import torch
+
+    rng = np.random.default_rng(11)
+    for nbytes in (16, 4096 + 48, 3 << 20):
+        buf = torch.from_numpy(rng.integers(0, 256, size=nbytes, dtype=np.uint8)).to("cuda:0")
+        before = buf.clone()
+        sink = torch.zeros(4, dtype=torch.uint8, device="cuda:0")
+        say(f"read reference {nbytes} bytes")
+        pirscan.kernel_timer_begin(2)
+        pirscan.bench_read(buf, sink)
+        pirscan.bench_read(buf, sink)
+        kms = pirscan.kernel_timer_end(2)
+        assert len(kms) == 2 and all(k > 0.0 for k in kms)
+        assert torch.equal(buf, before)
+    with pytest.raises(pirscan.PirscanError):
+        pirscan.bench_read(buf[:20], sink)   # not a multiple of 16 bytes

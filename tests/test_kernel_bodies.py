@@ -13,7 +13,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = [os.path.join(ROOT, "he_database_scan_amd", "csrc", f)
-           for f in ("rowsel.hip", "rowsel_mfma.hip", "scalar.hip", "ntt.hip")] + \
+           for f in ("rowsel.hip", "rowsel_mfma.hip", "scalar.hip", "ntt.hip", "readprobe.hip")] + \
           [os.path.join(ROOT, "synth", "synth.hip")]
 HIPCC = "/opt/rocm/bin/hipcc"
 
