@@ -546,6 +546,9 @@ hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint
 #ifndef PIRSCAN_TGEMV_RING
 #define PIRSCAN_TGEMV_RING 2
 #endif
+#ifndef PIRSCAN_TGEMV_WINDOW_STEPS
+#define PIRSCAN_TGEMV_WINDOW_STEPS 128  // k-block per workgroup (0: one resident long share per wave)
+#endif
 constexpr int kTiledGemvTiles = PIRSCAN_TGEMV_TILES;
 constexpr int kTiledGemvRing = PIRSCAN_TGEMV_RING;
 constexpr uint64_t kTiledGemvTargetWaves = PIRSCAN_TGEMV_WAVES;  // 4 per SIMD
@@ -558,9 +561,21 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const u32x4* __res
   constexpr int TG = kTiledGemvTiles;
   const uint32_t lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane % 16, lg = lane / 16;
-  const uint64_t item = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
-  if (item >= items) return;  // no barriers in this kernel
-  const uint64_t kb = item % nkb, tg = item / nkb;
+  uint64_t kb, tg;
+  if constexpr (PIRSCAN_TGEMV_WINDOW_STEPS > 0) {
+    static_assert(4 * kTiledGemvTiles == kScalarGroupTiles, "a workgroup is one tile group");
+    // workgroup = the 16 row tiles of one group x one k-block, in address
+    // order: the k-blocks in flight form one window moving through the DB
+    const uint64_t wg = blockIdx.x;
+    kb = wg % nkb;
+    tg = (wg / nkb) * 4 + wave;
+    if (tg * nkb >= items) return;  // no barriers in this kernel
+  } else {
+    const uint64_t item = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
+    if (item >= items) return;  // no barriers in this kernel
+    kb = item % nkb;
+    tg = item / nkb;
+  }
   const uint64_t s0 = kb * kblock_steps;
   const uint64_t nst = (s0 + kblock_steps < psteps ? s0 + kblock_steps : psteps) - s0;  // >= 1
   const u32x4* frag[TG];
@@ -788,7 +803,8 @@ bool scalar_tiled_plan(uint64_t M, uint64_t K, uint32_t B, ScalarPlan* p) {
   p->bpad = 1;
   const uint64_t psteps = ceil_div(K, 64);
   const uint64_t waves = ceil_div(ceil_div(M, 16), kTiledGemvTiles);
-  uint64_t nkb = ceil_div(kTiledGemvTargetWaves, waves);
+  uint64_t nkb = PIRSCAN_TGEMV_WINDOW_STEPS > 0 ? ceil_div(psteps, PIRSCAN_TGEMV_WINDOW_STEPS)
+                                                : ceil_div(kTiledGemvTargetWaves, waves);
   if (nkb > psteps) nkb = psteps;
   p->kblock = ceil_div(psteps, nkb) * 64;
   p->nkb = ceil_div(psteps * 64, p->kblock);
