@@ -117,12 +117,12 @@ def test_scalar_tiled_sizes_and_validation():
     assert pirscan.scalar_layout_db_bytes(1, 1) == 16 * 1024
     assert pirscan.scalar_layout_db_bytes(0, 5) == 0 and pirscan.scalar_layout_db_bytes(5, 0) == 0
     # B > 1: the MFMA plan's digit planes of up to 64 columns and split-K
-    # partials; B = 1: 4 digit bytes per k (and one 64-k step of zeros), K
-    # split while the row tiles are too few to fill the GPU (4096 wavefronts
-    # of 4 tiles)
+    # partials; B = 1: 4 digit bytes per k (and one 64-k step of zeros) and
+    # one partial sum per row for each k-block of 128 steps (8192 k)
     assert pirscan.scalar_tiled_workspace_bytes(262144, 262144, 32) == 262144 * 128
-    assert pirscan.scalar_tiled_workspace_bytes(262144, 262144, 1) == (262144 + 64) * 4   # + one zero step
-    assert pirscan.scalar_tiled_workspace_bytes(32768, 32768, 1) == (32768 + 64) * 4 + 8 * 32768 * 4
+    assert pirscan.scalar_tiled_workspace_bytes(262144, 262144, 1) == (262144 + 64) * 4 + 32 * 262144 * 4
+    assert pirscan.scalar_tiled_workspace_bytes(32768, 32768, 1) == (32768 + 64) * 4 + 4 * 32768 * 4
+    assert pirscan.scalar_tiled_workspace_bytes(4096, 8192, 1) == (8192 + 64) * 4   # one k-block: no partials
     assert pirscan.scalar_tiled_workspace_bytes(0, 16, 1) == 0
     L = pirscan.lib()
     A = 1 << 40   # never dereferenced: every call below fails validation first
