@@ -4,9 +4,11 @@
  * passages of the pages each function restates.
  *
  * Style rule for this file: each function is the definition written out as
- * loops, in the pages' index order.  Threads split only the outermost
- * independent index (points for RowSel and ExpPack, rows for the scalar
- * product); they
+ * loops.  Every output is its own exact sum, taken over the summed index in
+ * the pages' order (k, i) and reduced once; only the order in which the
+ * independent outputs are visited is chosen, so that the contiguous index of
+ * each array runs innermost.  Threads split only the outermost independent
+ * index (points for RowSel and ExpPack, rows for the scalar product); they
  * never change the order or the exactness of any sum.
  */
 #include "oracle.h"
@@ -31,6 +33,24 @@ static int clamp_threads(int nthreads, uint64_t work_items) {
   return nthreads;
 }
 
+/* Runs worker(job t) on thread t (job 0 on the calling thread) and joins
+ * them; -1 if a thread could not start or a worker reported failure. */
+static int run_workers(pthread_t *th, int nthreads, void *(*worker)(void *), void *jobs, size_t job_size) {
+  char *base = (char *)jobs;
+  int rc = 0, started = 1;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, worker, base + (size_t)t * job_size) != 0) { rc = -1; break; }
+    ++started;
+  }
+  if (worker(base) != NULL) rc = -1;
+  for (int t = 1; t < started; ++t) {
+    void *ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret != NULL) rc = -1;
+  }
+  return rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* RowSel                                                                   */
 /* ------------------------------------------------------------------------ */
@@ -46,21 +66,31 @@ typedef struct {
 
 static void *rowsel_worker(void *arg) {
   const rowsel_job *j = (const rowsel_job *)arg;
-  const uint64_t P = j->P;
-  for (uint64_t p = j->p_begin; p < j->p_end; ++p) {
-    const uint64_t qr = j->q[p / j->N];
+  const uint64_t P = j->P, np = j->p_end - j->p_begin;
+  /* One exact 128-bit sum per output.  The free indices run n outermost and
+   * p innermost (the contiguous index of the p-major arrays), so every DB word
+   * is read once; each sum still takes k = 0 .. D0-1 in order. */
+  u128 *acc = (u128 *)malloc(sizeof(u128) * ((uint64_t)j->m * np + 1));
+  if (!acc) return (void *)1;
+  for (uint32_t n = 0; n < j->D1; ++n) {
+    for (uint64_t t = 0; t < (uint64_t)j->m * np; ++t) acc[t] = 0;
+    for (uint32_t k = 0; k < j->D0; ++k) {
+      const uint32_t *b = j->db + ((uint64_t)k * j->D1 + n) * P + j->p_begin;
+      for (uint32_t mi = 0; mi < j->m; ++mi) {
+        const uint32_t *a = j->ct + ((uint64_t)mi * j->D0 + k) * P + j->p_begin;
+        u128 *s = acc + (uint64_t)mi * np;
+        for (uint64_t t = 0; t < np; ++t) s[t] += (u128)((uint64_t)a[t] * b[t]);
+      }
+    }
     for (uint32_t mi = 0; mi < j->m; ++mi) {
-      for (uint32_t n = 0; n < j->D1; ++n) {
-        u128 acc = 0;
-        for (uint32_t k = 0; k < j->D0; ++k) {
-          const uint64_t a = j->ct[((uint64_t)mi * j->D0 + k) * P + p];
-          const uint64_t b = j->db[((uint64_t)k * j->D1 + n) * P + p];
-          acc += (u128)a * b;
-        }
-        j->out[((uint64_t)mi * j->D1 + n) * P + p] = (uint32_t)(acc % qr);
+      uint32_t *o = j->out + ((uint64_t)mi * j->D1 + n) * P;
+      for (uint64_t t = 0; t < np; ++t) {
+        const uint64_t p = j->p_begin + t;
+        o[p] = (uint32_t)(acc[(uint64_t)mi * np + t] % j->q[p / j->N]);
       }
     }
   }
+  free(acc);
   return NULL;
 }
 
@@ -82,12 +112,10 @@ int oracle_rowsel(const uint32_t *ct, const uint32_t *db, uint32_t *out,
     j->p_begin = P * (uint64_t)t / (uint64_t)nthreads;
     j->p_end = P * (uint64_t)(t + 1) / (uint64_t)nthreads;
   }
-  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, rowsel_worker, &jobs[t]);
-  rowsel_worker(&jobs[0]);
-  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  int rc = run_workers(th, nthreads, rowsel_worker, jobs, sizeof(rowsel_job));
   free(th);
   free(jobs);
-  return 0;
+  return rc;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -105,23 +133,34 @@ typedef struct {
 
 static void *exppack_worker(void *arg) {
   const exppack_job *j = (const exppack_job *)arg;
-  const uint64_t P = j->P, cols = 2ull * j->B;
-  for (uint64_t p = j->p_begin; p < j->p_end; ++p) {
-    const uint64_t qr = j->q[p / j->N];
-    for (uint32_t r = 0; r < j->Dr; ++r) {
+  const uint64_t P = j->P, cols = 2ull * j->B, np = j->p_end - j->p_begin;
+  /* One exact 128-bit sum per output.  The free indices run r outermost and
+   * p innermost (the contiguous index of the p-major arrays), so every hint
+   * word is read once; each sum still takes i = 0 .. n-1 in order. */
+  u128 *acc = (u128 *)malloc(sizeof(u128) * (cols * np + 1));
+  if (!acc) return (void *)1;
+  for (uint32_t r = 0; r < j->Dr; ++r) {
+    for (uint64_t t = 0; t < cols * np; ++t) acc[t] = 0;
+    for (uint32_t i = 0; i < j->n; ++i) {
+      const uint32_t *h = j->H + ((uint64_t)r * j->n + i) * P + j->p_begin;
       for (uint64_t c = 0; c < cols; ++c) {
-        u128 acc = 0;
-        for (uint32_t i = 0; i < j->n; ++i) {
-          const uint64_t h = j->H[((uint64_t)r * j->n + i) * P + p];
-          const uint64_t x = j->C[((uint64_t)i * cols + c) * P + p];
-          acc += (u128)h * x;
-        }
+        const uint32_t *x = j->C + ((uint64_t)i * cols + c) * P + j->p_begin;
+        u128 *s = acc + c * np;
+        for (uint64_t t = 0; t < np; ++t) s[t] += (u128)((uint64_t)h[t] * x[t]);
+      }
+    }
+    for (uint64_t c = 0; c < cols; ++c) {
+      uint32_t *o = j->out + ((uint64_t)r * cols + c) * P;
+      for (uint64_t t = 0; t < np; ++t) {
+        const uint64_t p = j->p_begin + t;
+        u128 v = acc[c * np + t];
         /* (0 | G): the second column of client c/2 carries G */
-        if (j->G && (c & 1)) acc += j->G[((uint64_t)r * j->B + c / 2) * P + p];
-        j->out[((uint64_t)r * cols + c) * P + p] = (uint32_t)(acc % qr);
+        if (j->G && (c & 1)) v += j->G[((uint64_t)r * j->B + c / 2) * P + p];
+        o[p] = (uint32_t)(v % j->q[p / j->N]);
       }
     }
   }
+  free(acc);
   return NULL;
 }
 
@@ -143,12 +182,10 @@ int oracle_exppack(const uint32_t *H, const uint32_t *C, const uint32_t *G,
     j->p_begin = P * (uint64_t)t / (uint64_t)nthreads;
     j->p_end = P * (uint64_t)(t + 1) / (uint64_t)nthreads;
   }
-  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, exppack_worker, &jobs[t]);
-  exppack_worker(&jobs[0]);
-  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  int rc = run_workers(th, nthreads, exppack_worker, jobs, sizeof(exppack_job));
   free(th);
   free(jobs);
-  return 0;
+  return rc;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -166,16 +203,27 @@ typedef struct {
 
 static void *scalar_worker(void *arg) {
   const scalar_job *j = (const scalar_job *)arg;
+  /* One uint32 sum per output, wrapping mod 2^32.  For each row the free index
+   * b runs innermost (the contiguous index of Q); each sum still takes
+   * k = 0 .. K-1 in order. */
+  uint32_t *acc = (uint32_t *)malloc(sizeof(uint32_t) * ((uint64_t)j->B + 1));
+  if (!acc) return (void *)1;
   for (uint64_t i = j->i_begin; i < j->i_end; ++i) {
-    for (uint32_t b = 0; b < j->B; ++b) {
-      uint32_t acc = 0;
-      for (uint64_t k = 0; k < j->K; ++k) {
-        const uint32_t d = (uint32_t)(int32_t)j->db[i * j->K + k]; /* sign-extend */
-        acc += d * j->Q[k * j->B + b];                             /* wraps mod 2^32 */
-      }
-      j->out[i * j->B + b] = acc;
+    if (j->B == 1) { /* a single column: the sum stays in a register */
+      uint32_t s = 0;
+      for (uint64_t k = 0; k < j->K; ++k) s += (uint32_t)(int32_t)j->db[i * j->K + k] * j->Q[k];
+      j->out[i] = s;
+      continue;
     }
+    for (uint32_t b = 0; b < j->B; ++b) acc[b] = 0;
+    for (uint64_t k = 0; k < j->K; ++k) {
+      const uint32_t d = (uint32_t)(int32_t)j->db[i * j->K + k]; /* sign-extend */
+      const uint32_t *qk = j->Q + k * j->B;
+      for (uint32_t b = 0; b < j->B; ++b) acc[b] += d * qk[b];  /* wraps mod 2^32 */
+    }
+    for (uint32_t b = 0; b < j->B; ++b) j->out[i * j->B + b] = acc[b];
   }
+  free(acc);
   return NULL;
 }
 
@@ -192,12 +240,10 @@ int oracle_scalar(const int8_t *db, const uint32_t *Q, uint32_t *out,
     j->i_begin = M * (uint64_t)t / (uint64_t)nthreads;
     j->i_end = M * (uint64_t)(t + 1) / (uint64_t)nthreads;
   }
-  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, scalar_worker, &jobs[t]);
-  scalar_worker(&jobs[0]);
-  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+  int rc = run_workers(th, nthreads, scalar_worker, jobs, sizeof(scalar_job));
   free(th);
   free(jobs);
-  return 0;
+  return rc;
 }
 
 /* ------------------------------------------------------------------------ */
