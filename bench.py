@@ -615,6 +615,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    from he_database_scan_amd import pirscan
+
+    # the benchmark build: the product sources with the kernel-timing hooks
+    # (include/pirscan_bench.h), so each scan's main kernel is timed live
+    pirscan.use_library(pirscan.BENCH_LIB_PATH)
     w = Workloads()
     scans = w.scans()
     stream = torch.cuda.current_stream()

@@ -9,6 +9,7 @@
 namespace pirscan {
 
 constexpr int kMaxLimbs = 8;
+constexpr int kMaxDevices = 64;  // per-device caches cover device ids below this
 
 // Per-limb constants precomputed on the host for the RowSel kernels.
 struct LimbConsts {
@@ -39,6 +40,7 @@ struct RowselLaunch {
   uint64_t P;
   uint32_t N, D0, D1, m;
   uint32_t fold;           // products accumulated between two folds (>= 1)
+  uint32_t scan;           // PIRSCAN_SCAN_AUTO or PIRSCAN_SCAN_VALU (which kernel, which DB layout)
   LimbConsts lc;
 };
 
@@ -77,9 +79,13 @@ hipError_t launch_out_relayout(const RowselLaunch& a, const uint32_t* out_t, hip
 // RowSel / ExpPack on int8 MFMA over centred signed limbs, any m, with the
 // DB operand packed once into B-fragment order.  Usable when every q < 2^31
 // and D0 <= kPackedMaxD0 (the int32 limb diagonals cannot overflow); other
-// shapes keep the [P][D0][D1] layout and the VALU scan.
+// shapes, and shapes that ask for the VALU scan, keep the [P][D0][D1] layout
+// and the VALU scan.
 constexpr uint32_t kPackedMaxD0 = 16384;
 bool rowsel_packed_ok(const uint32_t* q, uint32_t R, uint32_t D0);
+// Largest m a RowSel call accepts (ExpPack: 2B), so every row-pass loop and
+// its 32-row steps stay far inside 32 bits.
+constexpr uint32_t kMaxRows = 1u << 31;
 // Bytes of the packed operand: per point ceil(D1/16) column tiles (rounded up
 // to a whole group of tiles) x ceil(D0/64) steps x 4 KiB.
 uint64_t packed_layout_bytes(uint64_t P, uint32_t D0, uint32_t D1);
@@ -171,15 +177,29 @@ hipError_t launch_ntt_plan(const NttDesc& d, void* plan, hipStream_t stream);
 hipError_t launch_ntt(const NttDesc& d, NttMode mode, const void* plan, const uint32_t* in, uint32_t* out,
                       uint64_t count, hipStream_t stream);
 
-// Benchmark hook (pirscan_kernel_timer_begin / _end): when the calling
-// thread has it on, the launchers bracket their main kernel with these two
-// calls, which record a HIP event pair on `stream`.  No-ops otherwise.
+// Benchmark hook (include/pirscan_bench.h, only in the build with
+// PIRSCAN_BENCH_HOOKS=1, libpirscan_bench.so): when the calling thread has it
+// on, the launchers bracket their main kernel with these two calls, which
+// record a HIP event pair on `stream`.  In the product build they are empty.
+#ifndef PIRSCAN_BENCH_HOOKS
+#define PIRSCAN_BENCH_HOOKS 0
+#endif
+#if PIRSCAN_BENCH_HOOKS
 void timer_mark_start(hipStream_t stream);
 void timer_mark_stop(hipStream_t stream);
-
 // Benchmark reference: one non-temporal 16-byte read pass over `bytes` of buf
 // (bytes % 16 == 0, buf 16-byte aligned), timed by the kernel-timer hook.
 hipError_t launch_read_stream(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
+#else
+inline void timer_mark_start(hipStream_t) {}
+inline void timer_mark_stop(hipStream_t) {}
+#endif
+
+// The C-ABI layer's device check (PIRSCAN_OK when the current device is a
+// gfx950, else a PIRSCAN_E* status) and its mapping of a HIP error to a
+// status (recording the error as the thread's last device error).
+int api_device_check();
+int api_device_status(hipError_t e);
 
 // s_waitcnt immediate: vmcnt = n (< 64), expcnt and lgkmcnt left unconstrained.
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }

@@ -5,7 +5,6 @@
 #include <string.h>
 
 #include <atomic>
-#include <new>
 
 #include "../../include/pirscan.h"
 #include "internal.hpp"
@@ -14,28 +13,8 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-// Benchmark hook state of one thread: `cap` event pairs, `count` recorded,
-// `open` while a start has no stop yet.
-struct KernelTimer {
-  bool on = false, open = false;
-  uint32_t cap = 0, count = 0;
-  hipEvent_t* start = nullptr;
-  hipEvent_t* stop = nullptr;
-};
-thread_local KernelTimer g_timer;
-
-void timer_release() {
-  for (uint32_t i = 0; i < g_timer.cap; ++i) {
-    (void)hipEventDestroy(g_timer.start[i]);
-    (void)hipEventDestroy(g_timer.stop[i]);
-  }
-  delete[] g_timer.start;
-  delete[] g_timer.stop;
-  g_timer = KernelTimer{};
-}
-
 // Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
-constexpr int kMaxDevices = 64;
+using pirscan::kMaxDevices;
 std::atomic<int> g_arch_ok[kMaxDevices];
 
 int device_check() {
@@ -80,6 +59,7 @@ unsigned __int128 packed_bytes_wide(unsigned __int128 P, uint32_t D0, uint32_t D
 // Validates a RowSel shape; on success returns P and the p-major DB word count.
 bool rowsel_shape_ok(const pirscan_rowsel_shape* s, uint64_t* P, uint64_t* db_words) {
   if (!s || s->N == 0 || s->R == 0 || s->R > PIRSCAN_MAX_R || s->D0 == 0 || s->D1 == 0) return false;
+  if (s->scan != PIRSCAN_SCAN_AUTO && s->scan != PIRSCAN_SCAN_VALU) return false;
   for (uint32_t r = 0; r < s->R; ++r)
     if (s->q[r] < 2) return false;
   const unsigned __int128 p = (unsigned __int128)s->R * s->N;
@@ -110,7 +90,8 @@ constexpr unsigned __int128 kMaxBytes = ~(uint64_t)0 >> 1;
 bool exppack_shape_ok(const pirscan_exppack_shape* s, uint32_t B, uint64_t* P, uint64_t* h_words,
                       uint64_t* c_words, uint64_t* g_words, uint64_t* o_words) {
   if (!s || s->N == 0 || s->R == 0 || s->R > PIRSCAN_MAX_R || s->Dr == 0 || s->n == 0) return false;
-  if (B > 0x7FFFFFFFu) return false;
+  if (s->scan != PIRSCAN_SCAN_AUTO && s->scan != PIRSCAN_SCAN_VALU) return false;
+  if (B > pirscan::kMaxRows / 2) return false;
   for (uint32_t r = 0; r < s->R; ++r)
     if (s->q[r] < 2) return false;
   const unsigned __int128 p = (unsigned __int128)s->R * s->N;
@@ -148,23 +129,28 @@ void exppack_launch_desc(const pirscan_exppack_shape* s, uint32_t B, uint64_t P,
   a->D0 = s->n;
   a->D1 = s->Dr;
   a->m = (uint32_t)cols;
+  a->scan = s->scan;
   fill_limb_consts(s->q, s->R, a);
 }
 
-// Whether the shape's DB / hint operand is packed for the MFMA scan (every
-// q < 2^31 and D0 <= 16384), or kept word-transposed for the VALU scan.
-bool packed_shape(const uint32_t* q, uint32_t R, uint32_t D0) { return pirscan::rowsel_packed_ok(q, R, D0); }
+// Whether the shape's DB / hint operand is packed for the MFMA scan (scan
+// kind AUTO with every q < 2^31 and D0 <= 16384), or kept word-transposed for
+// the VALU scan.
+bool packed_shape(const uint32_t* q, uint32_t R, uint32_t D0, uint32_t scan) {
+  return scan == PIRSCAN_SCAN_AUTO && pirscan::rowsel_packed_ok(q, R, D0);
+}
 
 // Bytes of the relaid DB / hint operand (D0 = reduction extent, D1 = columns).
-uint64_t operand_layout_bytes(const uint32_t* q, uint32_t R, uint64_t P, uint32_t D0, uint32_t D1) {
-  if (packed_shape(q, R, D0)) return pirscan::packed_layout_bytes(P, D0, D1);
+uint64_t operand_layout_bytes(const uint32_t* q, uint32_t R, uint64_t P, uint32_t D0, uint32_t D1,
+                              uint32_t scan) {
+  if (packed_shape(q, R, D0, scan)) return pirscan::packed_layout_bytes(P, D0, D1);
   return 4ull * P * D0 * D1;
 }
 
 // Workspace of the point-wise modular GEMM: the MFMA path's A fragments and
 // output staging, or the VALU path's output staging.
 size_t modgemm_workspace_bytes(const pirscan::RowselLaunch& a, uint32_t R) {
-  if (packed_shape(a.lc.q, R, a.D0)) return pirscan::rowsel_packed_workspace_bytes(a.P, a.m, a.D0, a.D1);
+  if (packed_shape(a.lc.q, R, a.D0, a.scan)) return pirscan::rowsel_packed_workspace_bytes(a.P, a.m, a.D0, a.D1);
   return pirscan::rowsel_valu_workspace_bytes(a.P, a.m, a.D1);
 }
 
@@ -181,7 +167,7 @@ int run_modgemm(const pirscan::RowselLaunch& a, uint32_t R, const Span* bufs, in
     return PIRSCAN_EINVAL;
   for (int i = 0; i < nbufs; ++i)
     if (overlap(workspace, need, bufs[i].p, bufs[i].bytes)) return PIRSCAN_EINVAL;
-  const bool packed = packed_shape(a.lc.q, R, a.D0);
+  const bool packed = packed_shape(a.lc.q, R, a.D0, a.scan);
   if (packed && (reinterpret_cast<uintptr_t>(a.dbt) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
@@ -277,16 +263,8 @@ int run_ntt(const pirscan_ntt_shape* s, pirscan::NttMode mode, const void* plan,
 
 namespace pirscan {
 
-void timer_mark_start(hipStream_t stream) {
-  if (!g_timer.on || g_timer.open || g_timer.count >= g_timer.cap) return;
-  if (hipEventRecord(g_timer.start[g_timer.count], stream) == hipSuccess) g_timer.open = true;
-}
-
-void timer_mark_stop(hipStream_t stream) {
-  if (!g_timer.on || !g_timer.open) return;
-  g_timer.open = false;
-  if (hipEventRecord(g_timer.stop[g_timer.count], stream) == hipSuccess) ++g_timer.count;
-}
+int api_device_check() { return device_check(); }
+int api_device_status(hipError_t e) { return device_status(e); }
 
 }  // namespace pirscan
 
@@ -295,15 +273,15 @@ extern "C" {
 size_t pirscan_layout_db_bytes(const pirscan_rowsel_shape* s) {
   uint64_t P = 0, words = 0;
   if (!rowsel_shape_ok(s, &P, &words)) return 0;
-  return (size_t)operand_layout_bytes(s->q, s->R, P, s->D0, s->D1);
+  return (size_t)operand_layout_bytes(s->q, s->R, P, s->D0, s->D1, s->scan);
 }
 
 int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor, uint32_t* db_tiled,
                       void* stream) {
   uint64_t P = 0, words = 0;
   if (!rowsel_shape_ok(s, &P, &words) || !db_pmajor || !db_tiled) return PIRSCAN_EINVAL;
-  const uint64_t tiled_bytes = operand_layout_bytes(s->q, s->R, P, s->D0, s->D1);
-  const bool packed = packed_shape(s->q, s->R, s->D0);
+  const uint64_t tiled_bytes = operand_layout_bytes(s->q, s->R, P, s->D0, s->D1, s->scan);
+  const bool packed = packed_shape(s->q, s->R, s->D0, s->scan);
   if (overlap(db_pmajor, words * 4, db_tiled, tiled_bytes)) return PIRSCAN_EINVAL;
   if (packed && (reinterpret_cast<uintptr_t>(db_tiled) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
@@ -321,7 +299,7 @@ static bool rowsel_launch_desc(const pirscan_rowsel_shape* s, uint32_t m, const 
                                const uint32_t* db_tiled, uint32_t* out, pirscan::RowselLaunch* a,
                                uint64_t* db_words, uint64_t* ct_words, uint64_t* out_words) {
   uint64_t P = 0;
-  if (!rowsel_shape_ok(s, &P, db_words) || m == 0) return false;
+  if (!rowsel_shape_ok(s, &P, db_words) || m == 0 || m > pirscan::kMaxRows) return false;
   const unsigned __int128 cw = (unsigned __int128)m * s->D0 * P;
   const unsigned __int128 ow = (unsigned __int128)m * s->D1 * P;
   if (cw * 4 > (unsigned __int128)(~(uint64_t)0 >> 1) || ow * 4 > (unsigned __int128)(~(uint64_t)0 >> 1))
@@ -341,6 +319,7 @@ static bool rowsel_launch_desc(const pirscan_rowsel_shape* s, uint32_t m, const 
   a->D0 = s->D0;
   a->D1 = s->D1;
   a->m = m;
+  a->scan = s->scan;
   fill_limb_consts(s->q, s->R, a);
   return true;
 }
@@ -359,7 +338,7 @@ int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint
   uint64_t dbw = 0, ctw = 0, ow = 0;
   if (!ct || !db_tiled || !out || !rowsel_launch_desc(s, m, ct, db_tiled, out, &a, &dbw, &ctw, &ow))
     return PIRSCAN_EINVAL;
-  const uint64_t db_bytes = operand_layout_bytes(s->q, s->R, a.P, s->D0, s->D1);
+  const uint64_t db_bytes = operand_layout_bytes(s->q, s->R, a.P, s->D0, s->D1, s->scan);
   if (overlap(out, ow * 4, ct, ctw * 4) || overlap(out, ow * 4, db_tiled, db_bytes)) return PIRSCAN_EINVAL;
   const Span ins[] = {{ct, ctw * 4}, {db_tiled, db_bytes}, {out, ow * 4}};
   return run_modgemm(a, s->R, ins, 3, workspace, workspace_bytes, stream);
@@ -368,15 +347,15 @@ int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint
 size_t pirscan_exppack_layout_h_bytes(const pirscan_exppack_shape* s) {
   uint64_t P, h, c, g, o;
   if (!exppack_shape_ok(s, 0, &P, &h, &c, &g, &o)) return 0;
-  return (size_t)operand_layout_bytes(s->q, s->R, P, s->n, s->Dr);
+  return (size_t)operand_layout_bytes(s->q, s->R, P, s->n, s->Dr, s->scan);
 }
 
 int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_pmajor,
                              uint32_t* h_tiled, void* stream) {
   uint64_t P, h, c, g, o;
   if (!exppack_shape_ok(s, 0, &P, &h, &c, &g, &o) || !h_pmajor || !h_tiled) return PIRSCAN_EINVAL;
-  const uint64_t tiled_bytes = operand_layout_bytes(s->q, s->R, P, s->n, s->Dr);
-  const bool packed = packed_shape(s->q, s->R, s->n);
+  const uint64_t tiled_bytes = operand_layout_bytes(s->q, s->R, P, s->n, s->Dr, s->scan);
+  const bool packed = packed_shape(s->q, s->R, s->n, s->scan);
   if (overlap(h_pmajor, h * 4, h_tiled, tiled_bytes)) return PIRSCAN_EINVAL;
   if (packed && (reinterpret_cast<uintptr_t>(h_tiled) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
@@ -415,7 +394,7 @@ int pirscan_exppack_modgemm(const pirscan_exppack_shape* s, uint32_t B, const ui
   if (B == 0 || !C || !h_tiled || !out || !exppack_shape_ok(s, B, &P, &hw, &cw, &gw, &ow))
     return PIRSCAN_EINVAL;
   const uint64_t gb = G ? gw * 4 : 0;
-  const uint64_t hb = operand_layout_bytes(s->q, s->R, P, s->n, s->Dr);
+  const uint64_t hb = operand_layout_bytes(s->q, s->R, P, s->n, s->Dr, s->scan);
   if (overlap(out, ow * 4, C, cw * 4) || overlap(out, ow * 4, h_tiled, hb) || overlap(out, ow * 4, G, gb))
     return PIRSCAN_EINVAL;
   pirscan::RowselLaunch a;
@@ -525,54 +504,6 @@ int pirscan_ntt_inverse(const pirscan_ntt_shape* s, const void* plan, const uint
 int pirscan_ntt_rns_forward(const pirscan_ntt_shape* s, const void* plan, const uint32_t* coeffs,
                             uint32_t* out, uint64_t count, void* stream) {
   return run_ntt(s, pirscan::NttMode::kRnsForward, plan, coeffs, out, count, stream);
-}
-
-int pirscan_kernel_timer_begin(uint32_t capacity) {
-  if (capacity == 0 || capacity > (1u << 20)) return PIRSCAN_EINVAL;
-  timer_release();
-  g_timer.start = new (std::nothrow) hipEvent_t[capacity];
-  g_timer.stop = new (std::nothrow) hipEvent_t[capacity];
-  if (!g_timer.start || !g_timer.stop) {
-    timer_release();
-    return PIRSCAN_EINVAL;
-  }
-  for (uint32_t i = 0; i < capacity; ++i) {
-    hipError_t e = hipEventCreate(&g_timer.start[i]);
-    if (e == hipSuccess) {
-      e = hipEventCreate(&g_timer.stop[i]);
-      if (e != hipSuccess) (void)hipEventDestroy(g_timer.start[i]);
-    }
-    if (e != hipSuccess) {
-      g_timer.cap = i;
-      timer_release();
-      return device_status(e);
-    }
-    g_timer.cap = i + 1;
-  }
-  g_timer.on = true;
-  return PIRSCAN_OK;
-}
-
-int pirscan_kernel_timer_end(float* ms, uint32_t max_count, uint32_t* count) {
-  if (!g_timer.on) return PIRSCAN_EINVAL;
-  const uint32_t n = g_timer.count < max_count ? g_timer.count : max_count;
-  int st = PIRSCAN_OK;
-  for (uint32_t i = 0; i < n && st == PIRSCAN_OK; ++i) {
-    hipError_t e = hipEventSynchronize(g_timer.stop[i]);
-    if (e == hipSuccess && ms) e = hipEventElapsedTime(&ms[i], g_timer.start[i], g_timer.stop[i]);
-    st = device_status(e);
-  }
-  if (count) *count = st == PIRSCAN_OK ? n : 0;
-  timer_release();
-  return st;
-}
-
-int pirscan_bench_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
-  if (!buf || !sink || bytes == 0 || bytes % 16 != 0) return PIRSCAN_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0) return PIRSCAN_EINVAL;
-  const int dc = device_check();
-  if (dc != PIRSCAN_OK) return dc;
-  return device_status(pirscan::launch_read_stream(buf, bytes, sink, (hipStream_t)stream));
 }
 
 const char* pirscan_strerror(int status) {

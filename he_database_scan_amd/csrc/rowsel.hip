@@ -468,7 +468,8 @@ hipError_t launch_rowsel(const RowselLaunch& a0, void* workspace, hipStream_t st
   RowselLaunch a = a0;
   a.out_t = static_cast<uint32_t*>(workspace);
   timer_mark_start(stream);
-  for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
+  for (uint64_t mb = 0; mb < a.m; mb += 32) {
+    const uint32_t m_base = (uint32_t)mb;
     const uint32_t rows = a.m - m_base;
     hipError_t e;
     if (rows <= 2) e = launch_mr<2, 1, 4>(a, m_base, stream);

@@ -598,9 +598,6 @@ hipError_t launch_scan_direct(const RowselLaunch& a, const MfmaEpilogue& ep, con
 }  // namespace
 
 bool rowsel_packed_ok(const uint32_t* q, uint32_t R, uint32_t D0) {
-#ifdef PIRSCAN_FORCE_VALU
-  return false;
-#endif
   if (D0 > kPackedMaxD0) return false;
   for (uint32_t r = 0; r < R; ++r)
     if (q[r] >= (1u << 31)) return false;
@@ -677,7 +674,8 @@ hipError_t launch_rowsel_packed(const RowselLaunch& a, uint32_t R, void* workspa
   }
 
   hipError_t e = hipSuccess;
-  for (uint32_t m_base = 0; m_base < a.m; m_base += 32) {
+  for (uint64_t mb = 0; mb < a.m; mb += 32) {
+    const uint32_t m_base = (uint32_t)mb;
     const uint32_t rows = a.m - m_base < 32 ? a.m - m_base : 32;
     const bool direct = rows <= kDirectRows;
     // ct rows m_base .. m_base + rows -> A fragments [p][s][row tile][limb][group][lane]:

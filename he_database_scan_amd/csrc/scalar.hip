@@ -25,6 +25,7 @@
 //    epilogue recombines the four digit planes with shifts, mod 2^32.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -506,6 +507,32 @@ uint32_t grid_for(uint64_t items, uint64_t cap = 1u << 20) {
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 uint64_t align_up(uint64_t a, uint64_t b) { return ceil_div(a, b) * b; }
 
+// Workgroups of mfma_kernel<NT, PACKED> the current device holds at once
+// (compute units x occupancy), queried once per device and kept.
+template <int NT, bool PACKED>
+hipError_t resident_workgroups(uint64_t* out) {
+  static std::atomic<uint64_t> cache[kMaxDevices];  // 0: not yet queried
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const uint64_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v) {
+      *out = v;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<NT, PACKED>, 64 * kMfmaWaves, 0);
+  if (e != hipSuccess) return e;
+  const uint64_t v = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)(per_cu > 0 ? per_cu : 1);
+  if (cached) cache[dev].store(v, std::memory_order_relaxed);
+  *out = v;
+  return hipSuccess;
+}
+
 template <int NT, bool PACKED>
 hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint64_t M, uint64_t K,
                        const ScalarPlan& pl, uint32_t bgroup, uint64_t ldd, uint32_t dcol0,
@@ -513,14 +540,10 @@ hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint
   const uint64_t rows_per_wg = kMfmaWaves * 16 * kMfmaRowTiles2;
   const uint64_t row_blocks = ceil_div(M, rows_per_wg);
   if (pl.kblock % kMfmaChunkK != 0) return hipErrorInvalidValue;
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<NT, PACKED>, 64 * kMfmaWaves, 0);
-  if (e != hipSuccess) return e;
   // persistent: as many workgroups as are co-resident, at least one per XCD
-  uint64_t grid = (uint64_t)cus * (uint64_t)(per_cu > 0 ? per_cu : 1);
+  uint64_t grid = 0;
+  const hipError_t e = resident_workgroups<NT, PACKED>(&grid);
+  if (e != hipSuccess) return e;
   if (grid > row_blocks * pl.nkb) grid = row_blocks * pl.nkb;
   if (grid < 8) grid = 8;
   hipLaunchKernelGGL((mfma_kernel<NT, PACKED>), dim3((uint32_t)grid), dim3(64 * kMfmaWaves), 0, stream, db,

@@ -32,8 +32,11 @@
  *    stream reaches that work.  The return value reports argument validation
  *    and launch only.
  *  - Status codes: PIRSCAN_OK (0) or a negative PIRSCAN_E* value.  No C++
- *    exception crosses this ABI.  Calls are thread-safe; the only global
- *    state is a lazily initialised, per-thread last HIP error.
+ *    exception crosses this ABI.  Calls are thread-safe.  The library's own
+ *    state is the calling thread's last HIP error and, per device, a cache
+ *    of whether the device is a gfx950 and of its compute-unit count and
+ *    kernel occupancy (filled on first use; nothing else persists between
+ *    calls).
  *  - All arithmetic is integer; results are exact (bit-identical to the
  *    definitions above).
  */
@@ -47,18 +50,33 @@
 extern "C" {
 #endif
 
-#define PIRSCAN_VERSION 10400 /* 1.4.0 */
+#define PIRSCAN_VERSION 20000 /* 2.0.0 */
 #define PIRSCAN_MAX_R 8
 
 enum {
   PIRSCAN_OK = 0,
   PIRSCAN_EINVAL = -1,       /* bad argument: null pointer, zero extent, modulus
-                                outside [2, 2^32), R > PIRSCAN_MAX_R, m == 0,
-                                output overlapping an input, workspace too small,
-                                size overflow */
+                                outside [2, 2^32), R > PIRSCAN_MAX_R, m out of
+                                range, unknown scan kind, output overlapping an
+                                input, workspace too small, size overflow */
   PIRSCAN_EDEVICE = -2,      /* a HIP call failed; see pirscan_last_device_error */
   PIRSCAN_EUNSUPPORTED = -3  /* current device is not gfx950 */
 };
+
+/*
+ * Which scan kernel a RowSel / ExpPack shape uses (the `scan` member of the
+ * shapes below).  Both give the same, exact result; they differ in speed and
+ * in the stored layout of the static operand, so the choice is part of the
+ * shape and must be the same for the one-time layout and every later scan.
+ *  PIRSCAN_SCAN_AUTO: the int8 matrix-core scan over centred signed limbs
+ *    (VIPIR section 4.1's INT8 decomposition) when every q[r] < 2^31 and the
+ *    reduction extent is <= 16384, else the VALU scan.
+ *  PIRSCAN_SCAN_VALU: always the VALU scan -- 32x32 -> 64-bit products with
+ *    lazy 64-bit accumulation and one reduction per output (VIPIR section
+ *    4.2) -- on a word-for-word transposed layout.
+ */
+#define PIRSCAN_SCAN_AUTO 0u
+#define PIRSCAN_SCAN_VALU 1u
 
 /*
  * Shape of one RowSel problem.  P = R*N points; point p belongs to RNS limb
@@ -73,15 +91,16 @@ typedef struct {
   uint32_t q[PIRSCAN_MAX_R];   /* moduli, each in [2, 2^32); q[r] for r >= R ignored */
   uint32_t D0;                 /* k extent */
   uint32_t D1;                 /* n extent */
+  uint32_t scan;               /* PIRSCAN_SCAN_AUTO (0) or PIRSCAN_SCAN_VALU */
 } pirscan_rowsel_shape;
 
 /* Bytes of the tiled RowSel database produced by pirscan_layout_db, or 0 if
- * the shape is invalid.  When every q[r] < 2^31 and D0 <= 16384 the database
- * is stored for the int8 matrix-core scan: per point, ceil(D1/16) column
+ * the shape is invalid.  For the int8 matrix-core scan (PIRSCAN_SCAN_AUTO
+ * with every q[r] < 2^31 and D0 <= 16384): per point, ceil(D1/16) column
  * tiles (rounded up to a multiple of 16 from 16 tiles on) x ceil(D0/64)
  * k-steps x 4 KiB (exactly 4 * P * D0 * D1 when 256 | D1 and 64 | D0, or
- * D1 = 16 * T with T < 16).  Otherwise it is stored word for word for the 64-bit VALU
- * scan: 4 * P * D0 * D1. */
+ * D1 = 16 * T with T < 16).  For the VALU scan the words are stored
+ * transposed, 4 * P * D0 * D1. */
 size_t pirscan_layout_db_bytes(const pirscan_rowsel_shape* s);
 
 /*
@@ -105,19 +124,19 @@ int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor,
 
 /*
  * Workspace bytes pirscan_rowsel_modgemm needs for (shape, m), 0 only on an
- * invalid shape or m == 0: the per-point staging of the output (4 * P * m *
- * D1 bytes) and, on the matrix-core scan (every q < 2^31, D0 <= 16384; GPIR:
- * batching makes RowSel a dense contraction, and at batch 1 the scan streams
- * the same bytes), the per-query limb split of ct: 16 * m bytes per point and
- * 64-k step for m <= 16, else 8 KiB (passes of 32 rows).  Each part is
- * rounded up to 256 bytes.
+ * invalid shape or m outside [1, 2^31]: the per-point staging of the output
+ * (4 * P * m * D1 bytes) and, on the matrix-core scan (GPIR: batching makes
+ * RowSel a dense contraction, and at batch 1 the scan streams the same
+ * bytes), the per-query limb split of ct: 16 * m bytes per point and 64-k
+ * step for m <= 16, else 8 KiB (passes of 32 rows).  Each part is rounded up
+ * to 256 bytes.
  */
 size_t pirscan_rowsel_workspace_bytes(const pirscan_rowsel_shape* s, uint32_t m);
 
 /*
  * RowSel scan: out[mi][n][p] = (sum_k ct[mi][k][p] * db[k][n][p]) mod q[p/N].
  *   m         : ciphertext polynomials in the query batch (m = 2B for B BFV
- *               ciphertexts of two polynomials each), m >= 1.
+ *               ciphertexts of two polynomials each), 1 <= m <= 2^31.
  *   ct        : [m][D0][P] uint32, p-major, entries < q[p/N].
  *   db_tiled  : output of pirscan_layout_db for the same shape.
  *   out       : [m][D1][P] uint32, p-major, canonical residues in [0, q[p/N]).
@@ -144,6 +163,7 @@ typedef struct {
   uint32_t q[PIRSCAN_MAX_R];   /* moduli, each in [2, 2^32); q[r] for r >= R ignored */
   uint32_t Dr;                 /* output ciphertexts, ceil(D1 / N): rows of H and G */
   uint32_t n;                  /* LWE dimension: columns of H, rows of C */
+  uint32_t scan;               /* PIRSCAN_SCAN_AUTO (0) or PIRSCAN_SCAN_VALU (reduction extent n) */
 } pirscan_exppack_shape;
 
 /* Bytes of the tiled hint produced by pirscan_exppack_layout_h, or 0 if the
@@ -169,7 +189,7 @@ int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_p
 /*
  * Workspace bytes pirscan_exppack_modgemm needs for (shape, B): as
  * pirscan_rowsel_workspace_bytes with m = 2B, D0 = n and D1 = Dr.  0 only on
- * an invalid shape or B == 0.
+ * an invalid shape or B outside [1, 2^30].
  */
 size_t pirscan_exppack_workspace_bytes(const pirscan_exppack_shape* s, uint32_t B);
 
@@ -177,8 +197,8 @@ size_t pirscan_exppack_workspace_bytes(const pirscan_exppack_shape* s, uint32_t 
  * ExpPack packing GEMM for B clients:
  *   out[r][j][p] = (sum_i H[r][i][p] * C[i][j][p] + Z[r][j][p]) mod q[p/N],
  *   Z[r][2b+1][p] = G[r][b][p], Z[r][2b][p] = 0.
- *   B         : clients, >= 1; client b owns columns 2b and 2b+1 of C and out
- *               (the two polynomials of its ciphertexts).
+ *   B         : clients, 1 <= B <= 2^30; client b owns columns 2b and 2b+1 of
+ *               C and out (the two polynomials of its ciphertexts).
  *   C         : [n][2B][P] uint32, p-major, entries < q[p/N]: the expanded
  *               special ciphertexts (n x 2B matrix of polynomials).
  *   h_tiled   : output of pirscan_exppack_layout_h for the same shape.
@@ -319,35 +339,6 @@ int pirscan_ntt_inverse(const pirscan_ntt_shape* s, const void* plan, const uint
  */
 int pirscan_ntt_rns_forward(const pirscan_ntt_shape* s, const void* plan, const uint32_t* coeffs,
                             uint32_t* out, uint64_t count, void* stream);
-
-/*
- * Benchmark hook for the calling thread (not part of the scan).
- * pirscan_kernel_timer_begin(capacity) makes the thread's next `capacity`
- * scan calls record a pair of HIP events on their stream around their main
- * kernel -- the scan kernel itself, without the per-query pre- and
- * post-passes (digit split, ct / output relayout, split-K reduction); the
- * passes of a batch wider than one kernel launch are timed as one interval.
- * pirscan_kernel_timer_end waits for the recorded events, writes the elapsed
- * milliseconds of each call, in call order, to the HOST array ms[0..*count)
- * (at most max_count entries) and turns the hook off.  The events belong to
- * the library.  Not for use under stream capture.  Returns PIRSCAN_EINVAL for
- * capacity 0 or > 2^20, or for _end without _begin.
- */
-int pirscan_kernel_timer_begin(uint32_t capacity);
-int pirscan_kernel_timer_end(float* ms, uint32_t max_count, uint32_t* count);
-
-/*
- * Benchmark reference (not part of the scan): one pass of 16-byte
- * non-temporal loads over `bytes` of the device buffer buf -- the access the
- * scans make to their databases, without their arithmetic -- so that a
- * scan's HBM rate can be compared with a plain read stream's on the same
- * device.  Timed by the kernel-timer hook like a scan call.  buf: device
- * memory, 16-byte aligned, bytes a non-zero multiple of 16, only read.
- * sink: device memory of at least 4 bytes that a thread may overwrite with
- * its running xor (which keeps the loads from being optimised away); its
- * contents are unspecified afterwards.  PIRSCAN_EINVAL otherwise.
- */
-int pirscan_bench_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* pirscan_strerror(int status);

@@ -144,6 +144,13 @@ def _device_lib():
     if _dev is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built (run __graft_entry__.build())")
+        # torch's bundled HIP runtime must open the device before the one this
+        # library links comes up (loaded first, the library's runtime later
+        # finds no device), so torch's starts first
+        import torch
+
+        if torch.cuda.is_available():
+            torch.cuda.init()
         L = ctypes.CDLL(_LIB_PATH)
         vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
         L.pirsynth_fill_residues.argtypes = [vp, u64, u64, u64, u32, u32, ctypes.POINTER(u32), vp]

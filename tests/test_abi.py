@@ -1,6 +1,7 @@
-"""The C-ABI library (no GPU needed): it loads, exports every function that
-include/pirscan.h declares, and rejects bad arguments before touching the
-device."""
+"""The C-ABI libraries (no GPU needed): libpirscan.so loads and exports
+exactly the functions include/pirscan.h declares; libpirscan_bench.so exports
+those and include/pirscan_bench.h's; both reject bad arguments before
+touching the device."""
 import ctypes
 import os
 import re
@@ -11,12 +12,22 @@ from he_database_scan_amd import pirscan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pirscan.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "pirscan_bench.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pirscan_[a-z0-9_]+)\s*\(", text)))
+
+
+def exported_functions(path):
+    """Names of the functions a shared library exports (its dynamic symbol
+    table), read with the ELF tools' nm."""
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", path], check=True, capture_output=True, text=True).stdout
+    return sorted(ln.split()[-1] for ln in out.splitlines() if ln.split()[-2:-1] == ["T"])
 
 
 def test_header_declares_the_boundary():
@@ -29,19 +40,36 @@ def test_header_declares_the_boundary():
                  "pirscan_exppack_workspace_bytes", "pirscan_exppack_modgemm",
                  "pirscan_ntt_plan_bytes", "pirscan_ntt_plan_init", "pirscan_ntt_forward",
                  "pirscan_ntt_inverse", "pirscan_ntt_rns_forward",
-                 "pirscan_kernel_timer_begin", "pirscan_kernel_timer_end", "pirscan_bench_read",
                  "pirscan_version", "pirscan_last_device_error"):
         assert want in names
+    assert declared_functions(BENCH_HEADER) == ["pirscan_bench_read", "pirscan_kernel_timer_begin",
+                                                "pirscan_kernel_timer_end"]
+    assert not set(names) & set(declared_functions(BENCH_HEADER))
 
 
-def test_library_exports_every_declared_symbol():
+def test_libraries_export_exactly_their_headers():
+    """The product library exports the scan surface only (no benchmark hooks,
+    no internal C++ symbols); the benchmark build adds pirscan_bench.h."""
+    assert exported_functions(pirscan.LIB_PATH) == declared_functions()
+    assert exported_functions(pirscan.BENCH_LIB_PATH) == sorted(declared_functions() +
+                                                                declared_functions(BENCH_HEADER))
     L = ctypes.CDLL(pirscan.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
+    assert not hasattr(L, "pirscan_kernel_timer_begin")
+
+
+def test_struct_layouts_match_the_header():
+    # N, R, q[8], D0, D1, scan / N, R, q[8], Dr, n, scan / N, R, q[8], psi[8]
+    assert ctypes.sizeof(pirscan.RowselShape) == 4 * 13
+    assert ctypes.sizeof(pirscan.ExppackShape) == 4 * 13
+    assert ctypes.sizeof(pirscan.NttShape) == 4 * 18
+    assert pirscan.RowselShape.scan.offset == 48 and pirscan.ExppackShape.scan.offset == 48
 
 
 def test_version_and_strerror():
-    assert pirscan.version() == 10400
+    assert pirscan.version() == 20000
+    assert pirscan.bench_library().version() == 20000
     assert pirscan.strerror(0) == "ok"
     assert "invalid" in pirscan.strerror(-1)
     assert "gfx950" in pirscan.strerror(-3)
@@ -70,6 +98,12 @@ def test_layout_bytes_and_invalid_shapes():
     b = pirscan.RowselShape.make(4, Q3, 4, 4)
     b.R = 9
     assert pirscan.layout_db_bytes(b) == 0
+    # the VALU scan on request: the word layout whatever the moduli
+    v = pirscan.RowselShape.make(16, Q3, 65, 17, scan=pirscan.SCAN_VALU)
+    assert pirscan.layout_db_bytes(v) == 4 * 48 * 65 * 17
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(4096, Q3, 1024, 1024, scan=pirscan.SCAN_VALU)) == \
+        51539607552
+    assert pirscan.layout_db_bytes(pirscan.RowselShape.make(16, Q3, 65, 17, scan=2)) == 0   # unknown kind
 
 
 def test_page_size_identities():
@@ -107,6 +141,15 @@ def test_rowsel_workspace_sizes():
     assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(16, Q3, 20000, 64), 32) == 4 * 48 * 32 * 64
     assert pirscan.rowsel_workspace_bytes(pirscan.RowselShape.make(1, [7], 1, 1), 1) == 256 + 256
     assert pirscan.rowsel_workspace_bytes(s, 0) == 0
+    # the VALU scan on request: the output staging only
+    v = pirscan.RowselShape.make(4096, Q3, 1024, 1024, scan=pirscan.SCAN_VALU)
+    assert pirscan.rowsel_workspace_bytes(v, 2) == 4 * P * 2 * 1024
+    assert pirscan.rowsel_workspace_bytes(v, 32) == 4 * P * 32 * 1024
+    # m up to 2^31 (passes of 32 rows stay inside 32 bits); beyond, invalid
+    one = pirscan.RowselShape.make(1, [7], 1, 1)
+    assert pirscan.rowsel_workspace_bytes(one, 1 << 31) > 0
+    assert pirscan.rowsel_workspace_bytes(one, (1 << 31) + 1) == 0
+    assert pirscan.rowsel_workspace_bytes(one, 0xFFFFFFF0) == 0
 
 
 def test_scalar_tiled_sizes_and_validation():
@@ -167,6 +210,7 @@ def test_rowsel_rejects_bad_arguments_without_a_device():
     assert _call_rowsel(s, 2, A, B, C, W, small - 1) == pirscan.EINVAL
     assert _call_rowsel(None, 2, A, B, C) == pirscan.EINVAL
     assert _call_rowsel(s, 0, A, B, C) == pirscan.EINVAL
+    assert _call_rowsel(s, 0xFFFFFFF0, A, B, C) == pirscan.EINVAL              # m past 2^31
     assert _call_rowsel(s, 2, 0, B, C) == pirscan.EINVAL
     assert _call_rowsel(s, 2, A, 0, C) == pirscan.EINVAL
     assert _call_rowsel(s, 2, A, B, 0) == pirscan.EINVAL
@@ -200,6 +244,11 @@ def test_exppack_sizes():
     assert pirscan.exppack_workspace_bytes(big, 1) == 4 * 4096 * 2 * 256
     assert pirscan.exppack_layout_h_bytes(big) == 4 * 4096 * 256 * 1280
     assert pirscan.exppack_workspace_bytes(s, 0) == 0
+    assert pirscan.exppack_workspace_bytes(s, (1 << 30) + 1) == 0            # 2B past 2^31
+    sv = pirscan.ExppackShape.make(4096, Q3, 256, 1280, scan=pirscan.SCAN_VALU)
+    assert pirscan.exppack_layout_h_bytes(sv) == 15 * (1 << 30)
+    assert pirscan.exppack_workspace_bytes(sv, 16) == 4 * P * 32 * 256
+    assert pirscan.exppack_layout_h_bytes(pirscan.ExppackShape.make(4096, Q3, 256, 1280, scan=7)) == 0
     for bad in (pirscan.ExppackShape.make(0, Q3, 4, 4), pirscan.ExppackShape.make(4, Q3, 0, 4),
                 pirscan.ExppackShape.make(4, Q3, 4, 0), pirscan.ExppackShape.make(4, [1], 4, 4)):
         assert pirscan.exppack_layout_h_bytes(bad) == 0
@@ -250,15 +299,16 @@ def test_scalar_rejects_bad_arguments_without_a_device():
     assert f(A, B, C, 1 << 40, 1 << 40, 1, W, need) == pirscan.EINVAL  # size overflow
 
 
-def test_binding_fails_loudly_without_library(monkeypatch):
-    monkeypatch.setattr(pirscan, "LIB_PATH", "/nonexistent/libpirscan.so")
-    monkeypatch.setattr(pirscan, "_lib", None)
+def test_binding_fails_loudly_without_library():
     with pytest.raises(RuntimeError):
-        pirscan.version()
+        pirscan.Library("/nonexistent/libpirscan.so").version()
+    # the benchmark hooks exist in the benchmark build only
+    with pytest.raises(RuntimeError):
+        pirscan.Library(pirscan.LIB_PATH).kernel_timer_begin(1)
 
 
 def test_kernel_timer_argument_checks():
-    L = pirscan.lib()
+    L = pirscan.bench_library().lib()
     assert L.pirscan_kernel_timer_begin(0) == pirscan.EINVAL
     assert L.pirscan_kernel_timer_begin((1 << 20) + 1) == pirscan.EINVAL
     n = ctypes.c_uint32(7)
@@ -267,7 +317,7 @@ def test_kernel_timer_argument_checks():
 
 def test_bench_read_argument_checks():
     """The read-stream reference validates before touching a device."""
-    L = pirscan.lib()
+    L = pirscan.bench_library().lib()
     vp = ctypes.c_void_p
     buf, sink = vp(1 << 20), vp(1 << 21)   # never dereferenced: every call below is rejected first
     assert L.pirscan_bench_read(None, 4096, sink, None) == pirscan.EINVAL
