@@ -1,16 +1,18 @@
 """ExpPack's packing GEMM H*C + (0|G) on the GPU through the C ABI,
 bit-exact against the oracle (VIPIR section 3.5.2).
 
-Element-by-element on shapes that cover both kernels (the VALU scan for
-2B < 16, int8 MFMA over centred limbs for 2B >= 16 and every q < 2^31),
-ragged Dr / n tails, multi-pass batches, G present and absent, and the
-moduli extremes; sampled points at the section 3.6 size (15 GiB hint)."""
+Element by element on shapes that cover both kernels (int8 MFMA over
+centred limbs whenever every q < 2^31 and n <= 16384; the 64-bit VALU scan
+for the moduli at or above 2^31), ragged Dr / n tails, multi-pass batches, G
+present and absent, and the moduli extremes; at the section 3.6 size (15 GiB
+hint) every output of B = 1 and B = 16."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
 from he_database_scan_amd import pirscan
+from tests.fullsize import check_modgemm
 from tests.gpu_util import MED_Q, TINY_Q, empty_bytes, empty_u32, release, say, to_dev_u32, to_host_u32
 
 pytestmark = pytest.mark.gpu
@@ -23,10 +25,10 @@ def workspace(shape, B):
     return torch.empty(n, dtype=torch.uint8, device="cuda:0") if n else None
 
 
-def run_gpu(H, C, G, N, q):
+def run_gpu(H, C, G, N, q, scan=pirscan.SCAN_AUTO):
     Dr, n, P = H.shape
     B = C.shape[1] // 2
-    shape = pirscan.ExppackShape.make(N, q, Dr, n)
+    shape = pirscan.ExppackShape.make(N, q, Dr, n, scan=scan)
     d_ht = empty_bytes(pirscan.exppack_layout_h_bytes(shape))
     pirscan.exppack_layout_h(shape, to_dev_u32(H), d_ht)
     d_out = empty_u32((Dr, 2 * B, P))
@@ -40,10 +42,10 @@ def rand_res(rng, shape, N, q):
     return (rng.integers(0, 1 << 63, size=shape, dtype=np.uint64) % qv).astype(np.uint32)
 
 
-# (Dr, n, B, with_G): VALU (2B = 2..14) and MFMA (2B = 16, 32, 34: two passes)
-# kernels, ragged Dr (column slices) and n (k tails past the LDS chunk, the
-# fold period and the 64-wide MFMA k-step), and the section 3.6 aspect
-# (Dr = 256, n = 1280) at a small N.
+# (Dr, n, B, with_G): the MFMA scan's batch classes (2B = 2..16 rows on the
+# direct kernel, 32 on the shared-ring kernel, 34 as a 32-row pass plus a
+# 2-row pass), ragged Dr (partial column tiles) and n (partial 64-wide
+# k-steps), and the section 3.6 aspect (Dr = 256, n = 1280) at a small N.
 SHAPES = [(3, 40, 1, True), (1, 1, 1, True), (256, 1280, 1, True), (5, 130, 2, False),
           (2, 1100, 3, True), (257, 33, 7, True), (5, 130, 8, True), (17, 65, 16, True),
           (9, 33, 17, True), (64, 1280, 16, False), (1, 1, 8, True)]
@@ -65,10 +67,10 @@ def test_shapes_full(Dr, n, B, with_g):
                                  ([2147483647, 2147483629], 8), ([3, 5], 16), (TINY_Q, 9),
                                  ([4294967291], 17)])
 def test_extreme_moduli_and_worst_case(q, B):
-    """Moduli near 2^32 (VALU, shortest fold), just under 2^31 (the MFMA
-    path's limit), tiny moduli, and a two-pass batch on the VALU scan (2B = 34
-    with a modulus >= 2^31); all-(q-1) inputs are the worst case of both the
-    64-bit accumulation and the limb diagonals."""
+    """Moduli near 2^32 (the VALU scan, shortest fold), just under 2^31 (the
+    MFMA path's limit), tiny moduli, and a two-pass batch on the VALU scan
+    (2B = 34 with a modulus >= 2^31); all-(q-1) inputs are the worst case of
+    both the 64-bit accumulation and the limb diagonals."""
     N, Dr, n = 4, 6, 97
     P = N * len(q)
     rng = np.random.default_rng(B + q[0] % 997)
@@ -84,6 +86,20 @@ def test_extreme_moduli_and_worst_case(q, B):
     np.testing.assert_array_equal(got[:, 0::2, :], np.broadcast_to((n % qv).astype(np.uint32), (Dr, B, P)))
     np.testing.assert_array_equal(got[:, 1::2, :],
                                   np.broadcast_to(((n + qv - 1) % qv).astype(np.uint32), (Dr, B, P)))
+
+
+@pytest.mark.parametrize("Dr,n,B", [(3, 40, 1), (257, 33, 7), (17, 65, 16), (9, 33, 17)])
+def test_valu_scan_on_request(Dr, n, B):
+    """scan = SCAN_VALU: the 64-bit VALU scan on the word-transposed hint with
+    moduli below 2^31, G present."""
+    N, q = 16, MED_Q
+    P = N * len(q)
+    rng = np.random.default_rng(900 + Dr * 10 + B)
+    say(f"exppack VALU on request Dr={Dr} n={n} B={B}")
+    H = rand_res(rng, (Dr, n, P), N, q)
+    C = rand_res(rng, (n, 2 * B, P), N, q)
+    G = rand_res(rng, (Dr, B, P), N, q)
+    np.testing.assert_array_equal(run_gpu(H, C, G, N, q, scan=pirscan.SCAN_VALU), oracle.exppack(H, C, G, N, q))
 
 
 @pytest.mark.parametrize("B", [1, 8])
@@ -122,25 +138,21 @@ def test_layout_h_is_a_permutation():
         assert not got[:, 1, :].any()
 
 
-def sampled_full_size(seed, B_list, points):
+def test_section_3_6_size_every_output():
     """VIPIR section 3.6's packing at full size (N = 2^12, #RNS = 3, Dr = 2^8,
-    n = 1280: a 15 GiB hint), synthesised on the device; the oracle regenerates
-    the inputs of the sampled points on the host."""
-    import torch
-
+    n = 1280: a 15 GiB hint) synthesised on the device, one tiled hint for
+    both batches, B = 1 and B = 16: every output.  The oracle reads the
+    device's own H, C and G back in chunks."""
     N, q, Dr, n = 4096, MED_Q, 256, 1280
     P = N * len(q)
+    seed = 6
     shape = pirscan.ExppackShape.make(N, q, Dr, n)
     say(f"exppack full size: synthesising {4 * P * Dr * n / 2**30:.1f} GiB hint")
     d_h = empty_u32((Dr, n, P))
     synth.fill_residues_(d_h, seed, synth.STREAM_EXPPACK_H, N, q)
     d_ht = empty_bytes(pirscan.exppack_layout_h_bytes(shape))
     pirscan.exppack_layout_h(shape, d_h, d_ht)
-    del d_h
-    release()
-    outs = {}
-    pts_t = torch.tensor(points, device="cuda:0")
-    for B in B_list:
+    for B in (1, 16):
         d_c = empty_u32((n, 2 * B, P))
         synth.fill_residues_(d_c, seed, synth.STREAM_EXPPACK_C, N, q)
         d_g = empty_u32((Dr, B, P))
@@ -148,25 +160,8 @@ def sampled_full_size(seed, B_list, points):
         d_out = empty_u32((Dr, 2 * B, P))
         say(f"  packing B={B}")
         pirscan.exppack_modgemm(shape, B, d_c, d_ht, d_g, d_out, workspace(shape, B))
-        outs[B] = to_host_u32(d_out.index_select(2, pts_t))
+        check_modgemm("exppack", (d_h,), {B: (d_c, d_g, d_out)}, N, q, [(0, P)], f"exppack 15 GiB B={B}")
         del d_c, d_g, d_out
-    del d_ht
+        release()
+    del d_h, d_ht
     release()
-    pts = np.asarray(points, dtype=np.uint64)
-    qs = [q[int(p) // N] for p in points]
-    r = np.arange(Dr, dtype=np.uint64)[:, None, None]
-    i = np.arange(n, dtype=np.uint64)[None, :, None]
-    H_s = synth.residues(seed, synth.STREAM_EXPPACK_H, (r * n + i) * P + pts, P, N, q)
-    for B, got in outs.items():
-        ii = np.arange(n, dtype=np.uint64)[:, None, None]
-        j = np.arange(2 * B, dtype=np.uint64)[None, :, None]
-        C_s = synth.residues(seed, synth.STREAM_EXPPACK_C, (ii * 2 * B + j) * P + pts, P, N, q)
-        b = np.arange(B, dtype=np.uint64)[None, :, None]
-        G_s = synth.residues(seed, synth.STREAM_EXPPACK_G, (r * B + b) * P + pts, P, N, q)
-        np.testing.assert_array_equal(got, oracle.exppack(H_s, C_s, G_s, 1, qs))
-
-
-def test_section_3_6_size_sampled():
-    """B = 1 (VALU) and B = 16 (MFMA) against one 15 GiB tiled hint."""
-    pts = [0, 1, 2, 3, 4095, 4096, 4097, 9000, 12286, 12287]
-    sampled_full_size(6, [1, 16], pts)

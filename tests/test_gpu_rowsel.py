@@ -1,8 +1,9 @@
 """RowSel on the GPU through the C ABI, bit-exact against the oracle.
 
-Element-by-element at sizes the oracle finishes in seconds (several
+Element by element at sizes the oracle finishes in seconds (several
 wavefront slices, ragged column / k tails, every row-group width and every
-fold period); sampled points at the full 3 GiB and 48 GiB configurations."""
+fold period).  The full 3 GiB and 48 GiB configurations are compared in
+test_gpu_rowsel_fullsize.py."""
 import numpy as np
 import pytest
 
@@ -14,10 +15,10 @@ from tests.gpu_util import MED_Q, TINY_Q, empty_bytes, empty_u32, release, say, 
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(ct, db, N, q):
+def run_gpu(ct, db, N, q, scan=pirscan.SCAN_AUTO):
     m, D0, P = ct.shape
     D1 = db.shape[1]
-    shape = pirscan.RowselShape.make(N, q, D0, D1)
+    shape = pirscan.RowselShape.make(N, q, D0, D1, scan=scan)
     d_db = to_dev_u32(db)
     d_dbt = empty_bytes(pirscan.layout_db_bytes(shape))
     pirscan.layout_db(shape, d_db, d_dbt)
@@ -106,6 +107,26 @@ def test_fold_periods_and_extreme_moduli(q):
     np.testing.assert_array_equal(run_gpu(ctm, dbm, N, q), oracle.rowsel(ctm, dbm, N, q))
 
 
+@pytest.mark.parametrize("m,D0,D1", [(1, 97, 260), (2, 1024, 64), (3, 40, 300), (6, 65, 129), (8, 17, 256),
+                                     (16, 70, 100), (17, 33, 64), (32, 66, 128), (40, 9, 33)])
+def test_valu_scan_on_request(m, D0, D1):
+    """scan = SCAN_VALU runs the 64-bit lazy-reduction kernel on the word
+    layout although every modulus is below 2^31: every row-group width, a
+    multi-pass m, ragged column slices and k tails past the fold period."""
+    rng = np.random.default_rng(5000 + m * 100 + D0)
+    N, q = 16, MED_Q
+    P = N * len(q)
+    say(f"rowsel VALU on request m={m} D0={D0} D1={D1}")
+    ct = rand_res(rng, (m, D0, P), N, q)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, q, scan=pirscan.SCAN_VALU), oracle.rowsel(ct, db, N, q))
+    qv = np.asarray(q, dtype=np.uint32)[np.arange(P) // N]
+    ctm = np.broadcast_to(qv - 1, (m, D0, P)).copy()
+    dbm = np.broadcast_to(qv - 1, (D0, D1, P)).copy()
+    got = run_gpu(ctm, dbm, N, q, scan=pirscan.SCAN_VALU)
+    assert (got == (D0 % qv)[None, None, :]).all()       # (q-1)^2 == 1: out = D0 mod q
+
+
 def test_repeat_runs_identical():
     rng = np.random.default_rng(1)
     N, m, D0, D1 = 16, 2, 50, 512
@@ -114,58 +135,6 @@ def test_repeat_runs_identical():
     a = run_gpu(ct, db, N, MED_Q)
     b = run_gpu(ct, db, N, MED_Q)
     np.testing.assert_array_equal(a, b)
-
-
-def sampled_full_size(seed, D0, D1, m, points, ct_stream=synth.STREAM_ROWSEL_CT):
-    """Full-size config synthesised on the device; the oracle regenerates the
-    inputs of the sampled points on the host and computes all their outputs."""
-    import torch
-
-    N, q = 4096, MED_Q
-    P = N * len(q)
-    shape = pirscan.RowselShape.make(N, q, D0, D1)
-    say(f"rowsel full size D0={D0} D1={D1} m={m}: synthesising {4 * P * D0 * D1 / 2**30:.1f} GiB")
-    d_db = empty_u32((D0, D1, P))
-    synth.fill_residues_(d_db, seed, synth.STREAM_ROWSEL_DB, N, q)
-    d_dbt = empty_bytes(pirscan.layout_db_bytes(shape))
-    pirscan.layout_db(shape, d_db, d_dbt)
-    del d_db
-    release()
-    outs = {}
-    for mm in m:
-        d_ct = empty_u32((mm, D0, P))
-        synth.fill_residues_(d_ct, seed, ct_stream, N, q)
-        d_out = empty_u32((mm, D1, P))
-        say(f"  scan m={mm}")
-        pirscan.rowsel_modgemm(shape, mm, d_ct, d_dbt, d_out, workspace(shape, mm))
-        pts = torch.tensor(points, device=d_out.device)
-        outs[mm] = to_host_u32(d_out.index_select(2, pts))
-        del d_ct, d_out
-    del d_dbt
-    release()
-    # host side: inputs of the sampled points only
-    pts = np.asarray(points, dtype=np.uint64)
-    qs = [q[int(p) // N] for p in points]
-    k = np.arange(D0, dtype=np.uint64)[:, None, None]
-    n = np.arange(D1, dtype=np.uint64)[None, :, None]
-    db_s = synth.residues(seed, synth.STREAM_ROWSEL_DB, (k * D1 + n) * P + pts[None, None, :], P, N, q)
-    for mm, got in outs.items():
-        mi = np.arange(mm, dtype=np.uint64)[:, None, None]
-        kk = np.arange(D0, dtype=np.uint64)[None, :, None]
-        ct_s = synth.residues(seed, ct_stream, (mi * D0 + kk) * P + pts[None, None, :], P, N, q)
-        want = oracle.rowsel(ct_s, db_s, 1, qs)
-        np.testing.assert_array_equal(got, want)
-
-
-def test_medium_config_sampled():
-    pts = [0, 1, 63, 64, 4095, 4096, 6000, 8191, 8192, 12287]
-    sampled_full_size(3, 256, 256, [2], pts)
-
-
-def test_large_config_sampled():
-    """48 GiB DB, B=1 (m=2) and B=16 (m=32) sharing one tiled DB."""
-    pts = [0, 1, 2, 3, 4095, 4096, 4097, 9000, 12286, 12287]
-    sampled_full_size(4, 1024, 1024, [2, 32], pts)
 
 
 # Batched path (m >= 16, every q < 2^31: int8 MFMA over centred signed limbs)

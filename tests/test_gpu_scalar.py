@@ -1,7 +1,8 @@
 """Scalar-HE product on the GPU through the C ABI, bit-exact against the
 oracle: element by element on multi-tile ragged shapes for the GEMV (B=1),
-MFMA (B>1) and generic paths; sampled rows at the full 1 GiB and 64 GiB
-configurations; overflow closed forms and one-hot selections."""
+MFMA (B>1) and generic paths; overflow closed forms and one-hot selections.
+The full 1 GiB and 64 GiB configurations are compared in
+test_gpu_scalar_fullsize.py."""
 import numpy as np
 import pytest
 
@@ -93,39 +94,6 @@ def test_one_hot_and_regev_view():
             np.testing.assert_array_equal(got[:, b], db[:, k].astype(np.int32).astype(np.uint32))
     got1 = run_gpu(db, Q[:, 2:3].copy())
     np.testing.assert_array_equal(got1[:, 0], got[:, 2])     # B=1 column == B>1 column
-
-
-def full_size_sampled(seed, M, K, Bs, rows):
-    import torch
-
-    say(f"scalar full size M={M} K={K}: synthesising {M * K / 2**30:.1f} GiB")
-    d_db = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
-    synth.fill_int8_(d_db, seed, synth.STREAM_SCALAR_DB)
-    db_s = synth.int8_rows(seed, synth.STREAM_SCALAR_DB, K, rows)
-    ridx = torch.tensor(rows, device="cuda:0")
-    for B in Bs:
-        say(f"  scan B={B}")
-        d_q = empty_u32((K, B))
-        synth.fill_uint32_(d_q, seed, synth.STREAM_SCALAR_Q)
-        d_o = empty_u32((M, B))
-        ws = torch.empty(pirscan.scalar_workspace_bytes(M, K, B), dtype=torch.uint8, device="cuda:0")
-        pirscan.scalar_gemm_u32(d_db, d_q, d_o, ws)
-        got = to_host_u32(d_o.index_select(0, ridx))
-        Q = synth.uint32_array(seed, synth.STREAM_SCALAR_Q, (K, B))
-        np.testing.assert_array_equal(got, oracle.scalar(db_s, Q))
-        del d_q, d_o, ws
-    del d_db
-    release()
-
-
-def test_scalar_1gib_sampled():
-    M = K = 32768
-    full_size_sampled(2, M, K, [1, 8], [0, 1, 63, 64, 255, 256, 10000, 32766, 32767])
-
-
-def test_scalar_64gib_sampled():
-    M = K = 262144
-    full_size_sampled(5, M, K, [1, 32], [0, 1, 63, 64, 131072, 200001, 262143])
 
 
 @pytest.mark.parametrize("B", [8, 32])

@@ -4,7 +4,8 @@ against the oracle: element by element on ragged shapes (M and K not
 multiples of the 16-row tile or the 64-byte step, misaligned row-major
 sources), every batch width class (1, several column tiles, several 64-column
 passes), closed forms past 2^31 inside one accumulator, one-hot selections,
-and sampled rows at the 64 GiB configuration."""
+and sampled rows of the hint and second-fold shapes (the 64 GiB configuration
+is compared in full in test_gpu_scalar_fullsize.py)."""
 import numpy as np
 import pytest
 
@@ -101,32 +102,6 @@ def test_tiled_one_hot_and_regev_view():
             np.testing.assert_array_equal(got[:, b], db[:, k].astype(np.int32).astype(np.uint32))
     got1 = run_gpu(db, Q[:, 6:7].copy())
     np.testing.assert_array_equal(got1[:, 0], got[:, 6])     # B = 1 column == the same column at B = 8
-
-
-def test_tiled_64gib_sampled():
-    """The 64 GiB configuration, B = 1 and 32, in the benchmark's launch
-    configuration (one tiled DB for both batches)."""
-    import torch
-
-    M = K = 262144
-    seed, rows = 5, [0, 1, 15, 16, 63, 64, 131072, 200001, 262143]
-    say("scalar tiled 64 GiB: synthesising")
-    d_db = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
-    synth.fill_int8_(d_db, seed, synth.STREAM_SCALAR_DB)
-    t = tiled(d_db)
-    del d_db
-    release()
-    db_s = synth.int8_rows(seed, synth.STREAM_SCALAR_DB, K, rows)
-    ridx = torch.tensor(rows, device="cuda:0")
-    for B in (1, 32):
-        say(f"  scan B={B}")
-        d_q = empty_u32((K, B))
-        synth.fill_uint32_(d_q, seed, synth.STREAM_SCALAR_Q)
-        got = to_host_u32(scan(t, M, K, d_q).index_select(0, ridx))
-        np.testing.assert_array_equal(got, oracle.scalar(db_s, synth.uint32_array(seed, synth.STREAM_SCALAR_Q, (K, B))))
-        del d_q
-    del t
-    release()
 
 
 def test_tiled_hint_and_second_fold_sampled():
