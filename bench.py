@@ -24,9 +24,20 @@ polynomials (N = 2^12, three primes) -- the fused RNS decomposition + forward
 transform of 5 GiB of integer coefficients, then the inverse and the forward
 transform in place on the 15 GiB of residues.
 
-The ``cpu_baseline`` leg times the CPU oracle (oracle/, plain C) on a bounded
-sample of each of the four scans and reports the oracle's DB-scan rate for the
-same step mix (and per scan, ExpPack included).
+Under ``config_rows``: the other configurations -- RowSel medium (3 GiB,
+B = 1) on the int8 matrix-core scan and on the VALU scan, scalar 1 GiB (B = 1
+and 8) on the tiled and the row-major entry points, the row-major entry point
+pirscan_scalar_gemm_u32 at 64 GiB (B = 1 and 32), and the 48 GiB RowSel DB on
+the VALU scan (B = 1 and 16) -- each timed the same way.
+
+The ``cpu_baseline`` leg times the CPU oracle (oracle/, plain C) on the host
+cores (count and CPU model reported) on bounded samples of the benchmark's own
+device inputs, copied back first (copy time reported apart), and reports the
+oracle's DB-scan rate for the same step mix, per scan, and on one thread for
+the tiny and 1 GiB configurations.
+
+The benchmark loads libpirscan_bench.so: the library's sources built with the
+kernel-timing hooks of include/pirscan_bench.h.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -81,13 +92,37 @@ SHAPE_SCANS = {
     "scalar_64GiB_D1_2e17_B1": (1 << 17, 1 << 19, 1),
     "scalar_64GiB_D1_2e17_B32": (1 << 17, 1 << 19, 32),
 }
-SEEDS = {"rowsel": 4, "scalar": 5, "exppack": 6, "ntt": 7}
+SEEDS = {"rowsel": 4, "scalar": 5, "exppack": 6, "ntt": 7, "scalar_1GiB": 2, "rowsel_medium": 3}
+# the other configurations, reported beside the step: RowSel medium (3 GiB,
+# D0 = D1 = 256, B = 1) on the matrix-core and on the VALU scan, scalar 1 GiB
+# (M = K = 32768, B = 1 and 8) on the tiled and the row-major entry points, the
+# row-major entry point at the 64 GiB configuration, and the 48 GiB RowSel DB
+# on the VALU scan (B = 1 and 16)
+RS_MED_D = 256
+SC_SMALL = 32768
+CPU_SAMPLE_POINTS = 64  # RowSel / ExpPack points the CPU baseline reads back (one RNS limb's first 64)
+CPU_SAMPLE_ROWS = 2048  # scalar DB rows the CPU baseline reads back (512 MiB)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "he_database_scan_amd", "csrc")
 # The source file of each scan's main kernel (traffic figures are dropped once
 # that file changes).
+CONFIG_SCANS = {  # name -> main kernel (the step's four scans are in SCAN_KERNELS below)
+    "scalar_64GiB_B1_rowmajor": "gemv_kernel",
+    "scalar_64GiB_B32_rowmajor": "mfma_kernel<8, false>",
+    "scalar_1GiB_B1": "gemv_tiled_kernel",
+    "scalar_1GiB_B8": "mfma_kernel<4, true>",
+    "scalar_1GiB_B1_rowmajor": "gemv_kernel",
+    "scalar_1GiB_B8_rowmajor": "mfma_kernel<4, false>",
+    "rowsel_3GiB_B1": "rowsel_packed_direct_kernel<1>",
+    "rowsel_3GiB_B1_valu": "rowsel_kernel<2, 1, 4, 8>",
+    "rowsel_48GiB_B1_valu": "rowsel_kernel<2, 1, 4, 8>",
+    "rowsel_48GiB_B16_valu": "rowsel_kernel<32, 2, 4, 4>",
+}
 KERNEL_SOURCES = {
+    **{name: os.path.join(_CSRC, "rowsel.hip" if "valu" in name else
+                          "rowsel_mfma.hip" if name.startswith("rowsel") else "scalar.hip")
+       for name in CONFIG_SCANS},
     "rowsel_48GiB_B1": os.path.join(_CSRC, "rowsel_mfma.hip"),
     "rowsel_48GiB_B16": os.path.join(_CSRC, "rowsel_mfma.hip"),
     "scalar_64GiB_B1": os.path.join(_CSRC, "scalar.hip"),
@@ -142,6 +177,9 @@ class Workloads:
         pirscan.layout_db(self.shape, db, self.dbt)
         torch.cuda.synchronize()
         self.layout_s = time.perf_counter() - t0
+        # the CPU baseline's sample: these points' p-major DB words, kept on the device
+        self.rs_sample_pts = (RS_N, RS_N + CPU_SAMPLE_POINTS)
+        self.rs_sample_db = db[:, :, self.rs_sample_pts[0]:self.rs_sample_pts[1]].contiguous()
         del db
         torch.cuda.empty_cache()
         self.ct, self.out, self.rws = {}, {}, {}
@@ -176,6 +214,7 @@ class Workloads:
         self.ht = torch.empty(pirscan.exppack_layout_h_bytes(self.eshape), dtype=torch.uint8, device=dev)
         pirscan.exppack_layout_h(self.eshape, h, self.ht)
         torch.cuda.synchronize()
+        self.ep_sample_h = h[:, :, self.rs_sample_pts[0]:self.rs_sample_pts[1]].contiguous()
         del h
         torch.cuda.empty_cache()
         self.ec, self.eg, self.eout, self.ews = {}, {}, {}, {}
@@ -248,6 +287,105 @@ class Workloads:
                          M * K, M * K + 4 * K * B + 4 * M * B, B, M * K * B, "scalar")
         return tiled, out
 
+    def rowmajor_scans(self):
+        """pirscan_scalar_gemm_u32 -- the row-major entry point -- on the 64 GiB
+        database's row-major bytes (the step scans the tiled copy)."""
+        torch, pz = self.torch, self.pirscan
+        dev = torch.device("cuda:0")
+        self.rm_bufs, out = [], {}
+        for B in (1, 32):
+            q = self.q[B]
+            o = torch.empty((SC_M, B), dtype=torch.int32, device=dev)
+            ws = torch.empty(max(16, pz.scalar_workspace_bytes(SC_M, SC_K, B)), dtype=torch.uint8, device=dev)
+            self.rm_bufs += [o, ws]
+            out[f"scalar_64GiB_B{B}_rowmajor"] = (
+                (lambda q=q, o=o, ws=ws: pz.scalar_gemm_u32(self.sdb, q, o, ws)),
+                SC_M * SC_K, SC_M * SC_K + 4 * SC_K * B + 4 * SC_M * B, B, SC_M * SC_K * B, "scalar")
+        return out
+
+    def small_config_scans(self):
+        """The two smaller configurations: scalar 1 GiB (M = K = 32768, B = 1
+        and 8, tiled and row-major entry points) and RowSel medium (N = 4096,
+        three primes, D0 = D1 = 256: 3 GiB, B = 1) on the matrix-core scan and
+        on the VALU scan (each with its own one-time layout)."""
+        torch, pz = self.torch, self.pirscan
+        import synth
+
+        dev = torch.device("cuda:0")
+        log("setup: scalar 1 GiB and RowSel 3 GiB configurations")
+        M = K = SC_SMALL
+        sd = torch.empty((M, K), dtype=torch.int8, device=dev)
+        synth.fill_int8_(sd, SEEDS["scalar_1GiB"], synth.STREAM_SCALAR_DB)
+        st = torch.empty(pz.scalar_layout_db_bytes(M, K), dtype=torch.uint8, device=dev)
+        pz.scalar_layout_db(sd, st)
+        self.small = {"sdb": sd, "sdbt": st}
+        out = {}
+        for B in (1, 8):
+            q = torch.empty((K, B), dtype=torch.int32, device=dev)
+            synth.fill_uint32_(q, SEEDS["scalar_1GiB"], synth.STREAM_SCALAR_Q)
+            o1 = torch.empty((M, B), dtype=torch.int32, device=dev)
+            o2 = torch.empty((M, B), dtype=torch.int32, device=dev)
+            w1 = torch.empty(pz.scalar_tiled_workspace_bytes(M, K, B), dtype=torch.uint8, device=dev)
+            w2 = torch.empty(max(16, pz.scalar_workspace_bytes(M, K, B)), dtype=torch.uint8, device=dev)
+            self.small[f"q{B}"] = q
+            self.small[f"bufs{B}"] = (o1, o2, w1, w2)
+            alg = M * K + 4 * K * B + 4 * M * B
+            out[f"scalar_1GiB_B{B}"] = ((lambda q=q, o=o1, w=w1: pz.scalar_gemm_u32_tiled(st, M, K, q, o, w)),
+                                        M * K, alg, B, M * K * B, "scalar")
+            out[f"scalar_1GiB_B{B}_rowmajor"] = ((lambda q=q, o=o2, w=w2: pz.scalar_gemm_u32(sd, q, o, w)),
+                                                 M * K, alg, B, M * K * B, "scalar")
+        P, D = RS_N * len(RS_Q), RS_MED_D
+        db = torch.empty((D, D, P), dtype=torch.int32, device=dev)
+        synth.fill_residues_(db, SEEDS["rowsel_medium"], synth.STREAM_ROWSEL_DB, RS_N, RS_Q)
+        ct = torch.empty((2, D, P), dtype=torch.int32, device=dev)
+        synth.fill_residues_(ct, SEEDS["rowsel_medium"], synth.STREAM_ROWSEL_CT, RS_N, RS_Q)
+        self.small["ct"] = ct
+        rs_db = 4 * P * D * D
+        for kind, suffix in ((pz.SCAN_AUTO, ""), (pz.SCAN_VALU, "_valu")):
+            shape = pz.RowselShape.make(RS_N, RS_Q, D, D, scan=kind)
+            dbt = torch.empty(pz.layout_db_bytes(shape), dtype=torch.uint8, device=dev)
+            pz.layout_db(shape, db, dbt)
+            o = torch.empty((2, D, P), dtype=torch.int32, device=dev)
+            ws = torch.empty(pz.rowsel_workspace_bytes(shape, 2), dtype=torch.uint8, device=dev)
+            self.small["rs" + suffix] = (shape, dbt, o, ws)
+            out["rowsel_3GiB_B1" + suffix] = (
+                (lambda shape=shape, dbt=dbt, o=o, ws=ws: pz.rowsel_modgemm(shape, 2, ct, dbt, o, ws)),
+                rs_db, rs_db + 4 * P * 2 * (D + D), 1, P * 2 * D * D, "rowsel")
+        torch.cuda.synchronize()
+        del db
+        torch.cuda.empty_cache()
+        return out
+
+    def valu48_scans(self):
+        """The 48 GiB RowSel DB on the VALU scan (PIRSCAN_SCAN_VALU: the word
+        layout and the 64-bit lazy-reduction kernel), B = 1 and 16.  Replaces
+        the packed DB of the step (freed first) with its word layout."""
+        torch, pz = self.torch, self.pirscan
+        import synth
+
+        dev = torch.device("cuda:0")
+        P = RS_N * len(RS_Q)
+        del self.dbt
+        torch.cuda.empty_cache()
+        log("setup: RowSel 48 GiB DB for the VALU scan (synthesise p-major, one-time word layout)")
+        self.vshape = pz.RowselShape.make(RS_N, RS_Q, RS_D0, RS_D1, scan=pz.SCAN_VALU)
+        db = torch.empty((RS_D0, RS_D1, P), dtype=torch.int32, device=dev)
+        synth.fill_residues_(db, SEEDS["rowsel"], synth.STREAM_ROWSEL_DB, RS_N, RS_Q)
+        self.vdbt = torch.empty(pz.layout_db_bytes(self.vshape), dtype=torch.uint8, device=dev)
+        pz.layout_db(self.vshape, db, self.vdbt)
+        torch.cuda.synchronize()
+        del db
+        torch.cuda.empty_cache()
+        rs_db = 4 * P * RS_D0 * RS_D1
+        out = {}
+        self.vws = {}
+        for m, B in ((2, 1), (32, 16)):
+            self.vws[m] = torch.empty(pz.rowsel_workspace_bytes(self.vshape, m), dtype=torch.uint8, device=dev)
+            out[f"rowsel_48GiB_B{B}_valu"] = (
+                (lambda m=m: pz.rowsel_modgemm(self.vshape, m, self.ct[m], self.vdbt, self.out[m], self.vws[m])),
+                rs_db, rs_db + 4 * P * m * (RS_D0 + RS_D1), B, P * m * RS_D0 * RS_D1, "rowsel")
+        return out
+
     # name -> (callable, DB bytes, algorithmic HBM bytes, queries, macs, kind)
     def scans(self):
         P = RS_N * len(RS_Q)
@@ -287,8 +425,12 @@ class Workloads:
 # multiplies 4 query digit planes; RowSel / ExpPack multiply 4 x 4 limb pairs,
 # and at m = 2 pad the 2 rows to a 16-row tile (x 8).
 MFMA_MACS_PER_MAC = {"rowsel_48GiB_B1": 128, "rowsel_48GiB_B16": 16, "scalar_64GiB_B32": 4,
-                     "exppack_15GiB_B1": 128, "exppack_15GiB_B16": 16,
+                     "exppack_15GiB_B1": 128, "exppack_15GiB_B16": 16, "rowsel_3GiB_B1": 128,
+                     "scalar_64GiB_B32_rowmajor": 4, "scalar_1GiB_B8": 8, "scalar_1GiB_B8_rowmajor": 8,
                      **{name: 4 for name, (M, K, B) in SHAPE_SCANS.items() if B > 1}}
+# scans on the VALU whose multiply work exceeds what HBM time allows: priced
+# against the v_mad_u64_u32 rate (one per 32x32 -> 64-bit product)
+VALU_BOUND = {"rowsel_48GiB_B16_valu"}
 # shapes whose int8 MFMA work exceeds what HBM time allows: priced against the MFMA peak
 MFMA_BOUND = {"scalar_hint_64GiB_n1280", "scalar_fold2_4GiB_n1281"}
 
@@ -307,6 +449,13 @@ def roofline_for(name, ms, db_bytes, alg_bytes, macs):
         tops = NTT_OPS_PER_BUTTERFLY * macs / (ms * 1e-3) / 1e12
         return {"bound": "alu", "achieved": tops, "peak": VALU_INT32_PEAK_TOPS, "unit": "TOP/s",
                 "frac": tops / VALU_INT32_PEAK_TOPS, "hbm_GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS}
+    if name in VALU_BOUND:
+        tmacs = macs / (ms * 1e-3) / 1e12
+        return {"bound": "valu", "achieved": tmacs, "peak": VALU_MAD64_PEAK_TMACS, "unit": "TMAC/s",
+                "frac": tmacs / VALU_MAD64_PEAK_TMACS, "hbm_GBps": achieved}
+    if name.endswith("_valu"):
+        rf["valu_mad64_TMACs"] = macs / (ms * 1e-3) / 1e12
+        rf["valu_frac"] = rf["valu_mad64_TMACs"] / VALU_MAD64_PEAK_TMACS
     if name in MFMA_BOUND:
         tops = 2 * macs * MFMA_MACS_PER_MAC[name] / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": tops, "peak": MFMA_INT8_PEAK_TOPS, "unit": "TOP/s",
@@ -345,8 +494,13 @@ SCAN_KERNELS = {
     "scalar_64GiB_B32": "mfma_kernel<8, true>",
     "exppack_15GiB_B1": "rowsel_packed_direct_kernel<1>",
     "exppack_15GiB_B16": "rowsel_packed_kernel<2, 2",
+    **{name: CONFIG_SCANS[name] for name in ("scalar_64GiB_B1_rowmajor", "scalar_64GiB_B32_rowmajor",
+                                             "scalar_1GiB_B1", "scalar_1GiB_B1_rowmajor", "scalar_1GiB_B8",
+                                             "scalar_1GiB_B8_rowmajor", "rowsel_3GiB_B1", "rowsel_3GiB_B1_valu")},
     **{name: ("gemv_tiled_kernel" if B == 1 else "mfma_kernel<8, true>" if B <= 32 else "mfma_kernel<16, true>")
        for name, (M, K, B) in SHAPE_SCANS.items()},
+    "rowsel_48GiB_B1_valu": CONFIG_SCANS["rowsel_48GiB_B1_valu"],
+    "rowsel_48GiB_B16_valu": CONFIG_SCANS["rowsel_48GiB_B16_valu"],
     "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
     "ntt_inv_hint": "ntt_kernel<12, true>",
     "ntt_fwd_hint": "ntt_kernel<12, false>",
@@ -434,82 +588,132 @@ def summarize_trace(trace_csv: str) -> str:
     return "\n".join(lines)
 
 
-def cpu_baseline(budget_s: float = 4.0):
-    """Times the oracle on bounded samples of the four scans (host cores) and
-    returns its DB-scan rate for the benchmark's step mix.  Each sample is
-    generated once (untimed) and the oracle's compute call is repeated until
-    about ``budget_s`` seconds have been spent on it."""
-    import numpy as np
+def host_info():
+    """The host this run is on: logical CPUs (hardware concurrency), what
+    `nproc` reports for this process, the threads the oracle uses (the
+    process's affinity set, capped by OMP_NUM_THREADS when set: the machine's
+    CPU share) and the CPU model."""
+    import subprocess
+
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True, check=True).stdout)
+    except (OSError, ValueError, subprocess.CalledProcessError):
+        nproc = None
+    threads = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        threads = min(threads, int(cap))
+    return {"hardware_concurrency": os.cpu_count(), "nproc": nproc, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads": cap or None, "threads_used": threads, "cpu_model": model}
+
+
+def cpu_baseline(w, budget_s: float = 2.0):
+    """Times the CPU oracle (oracle/, plain C) on this machine's host cores, on
+    bounded samples of the benchmark's own device inputs.  Each sample is
+    copied back from device memory (the copy timed on its own), then the
+    oracle's compute call is repeated until about ``budget_s`` seconds have
+    been spent on it; only the compute is timed.  Also times the whole tiny
+    RowSel and scalar 1 GiB configurations on one thread.  Returns (per-scan
+    oracle rates in DB bytes/s on all threads, host info, sample text,
+    device-to-host copy figures, single-thread rates)."""
+    import torch
 
     import oracle
     import synth
 
-    threads = min(16, os.cpu_count() or 1)
-    P = RS_N * len(RS_Q)
+    host = host_info()
+    threads = host["threads_used"]
+    a, b = w.rs_sample_pts
+    npts, qr = b - a, [RS_Q[a // RS_N]]
+    copies = {"bytes": 0, "s": 0.0}
 
-    def rowsel_sample(m, npts):
-        pts = np.linspace(0, P - 1, npts).astype(np.uint64)
-        k = np.arange(RS_D0, dtype=np.uint64)[:, None, None]
-        n = np.arange(RS_D1, dtype=np.uint64)[None, :, None]
-        db = synth.residues(SEEDS["rowsel"], synth.STREAM_ROWSEL_DB, (k * RS_D1 + n) * P + pts, P, RS_N, RS_Q)
-        mi = np.arange(m, dtype=np.uint64)[:, None, None]
-        kk = np.arange(RS_D0, dtype=np.uint64)[None, :, None]
-        ct = synth.residues(SEEDS["rowsel"], synth.STREAM_ROWSEL_CT, (mi * RS_D0 + kk) * P + pts, P, RS_N, RS_Q)
-        qs = [RS_Q[int(p) // RS_N] for p in pts]
-        return (lambda: oracle.rowsel(ct, db, 1, qs, nthreads=threads)), 4 * npts * RS_D0 * RS_D1, \
-            f"{npts} points x {RS_D0}x{RS_D1}, m={m}"
+    def fetch(t):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h = t.contiguous().cpu()
+        copies["s"] += time.perf_counter() - t0
+        copies["bytes"] += h.numel() * h.element_size()
+        return h.numpy()
 
-    def scalar_sample(B, rows):
-        db = synth.int8_rows(SEEDS["scalar"], synth.STREAM_SCALAR_DB, SC_K, range(rows))
-        Q = synth.uint32_array(SEEDS["scalar"], synth.STREAM_SCALAR_Q, (SC_K, B))
-        return (lambda: oracle.scalar(db, Q, nthreads=threads)), rows * SC_K, f"{rows} rows x {SC_K}, B={B}"
+    def u32(t):
+        return fetch(t).view("uint32")
 
-    def exppack_sample(B, npts):
-        pts = np.linspace(0, P - 1, npts).astype(np.uint64)
-        r = np.arange(EP_DR, dtype=np.uint64)[:, None, None]
-        i = np.arange(EP_N, dtype=np.uint64)[None, :, None]
-        H = synth.residues(SEEDS["exppack"], synth.STREAM_EXPPACK_H, (r * EP_N + i) * P + pts, P, RS_N, RS_Q)
-        ii = np.arange(EP_N, dtype=np.uint64)[:, None, None]
-        j = np.arange(2 * B, dtype=np.uint64)[None, :, None]
-        C = synth.residues(SEEDS["exppack"], synth.STREAM_EXPPACK_C, (ii * 2 * B + j) * P + pts, P, RS_N, RS_Q)
-        b = np.arange(B, dtype=np.uint64)[None, :, None]
-        G = synth.residues(SEEDS["exppack"], synth.STREAM_EXPPACK_G, (r * B + b) * P + pts, P, RS_N, RS_Q)
-        qs = [RS_Q[int(p) // RS_N] for p in pts]
-        return (lambda: oracle.exppack(H, C, G, 1, qs, nthreads=threads)), 4 * npts * EP_DR * EP_N, \
-            f"{npts} points x {EP_DR}x{EP_N}, B={B}"
-
-    def ntt_sample(kind, npolys):
-        R = len(RS_Q)
-        idx = np.linspace(0, NTT_COUNT - 1, npolys).astype(np.uint64)
-        coef = np.stack([synth.uint32_words(SEEDS["ntt"], synth.STREAM_NTT_IN,
-                                            np.arange(i * RS_N, (i + 1) * RS_N, dtype=np.uint64)) for i in idx])
-        res = oracle.ntt_rns(coef, RS_Q, NTT_PSI, nthreads=threads)
-        fn = {"rns": lambda: oracle.ntt_rns(coef, RS_Q, NTT_PSI, nthreads=threads),
-              "inv": lambda: oracle.ntt_batch(res, RS_Q, NTT_PSI, inverse=True, nthreads=threads),
-              "fwd": lambda: oracle.ntt_batch(res, RS_Q, NTT_PSI, nthreads=threads)}[kind]
-        return fn, 4 * npolys * R * RS_N, f"{npolys} polynomials x {R} limbs x N={RS_N}"
-
-    rates, samples = {}, []
-    for name, make in (("rowsel_48GiB_B1", lambda: rowsel_sample(2, threads)),
-                       ("rowsel_48GiB_B16", lambda: rowsel_sample(32, threads)),
-                       ("scalar_64GiB_B1", lambda: scalar_sample(1, 4 * threads)),
-                       ("scalar_64GiB_B32", lambda: scalar_sample(32, threads)),
-                       ("exppack_15GiB_B1", lambda: exppack_sample(1, threads)),
-                       ("exppack_15GiB_B16", lambda: exppack_sample(16, threads)),
-                       ("ntt_rns_fwd_hint", lambda: ntt_sample("rns", threads)),
-                       ("ntt_inv_hint", lambda: ntt_sample("inv", threads)),
-                       ("ntt_fwd_hint", lambda: ntt_sample("fwd", threads))):
-        fn, nbytes, what = make()
+    def timed(fn):
         reps, t0 = 0, time.perf_counter()
         while True:
             fn()
             reps += 1
             dt = time.perf_counter() - t0
             if dt >= budget_s:
-                break
-        rates[name] = reps * nbytes / dt
-        samples.append(f"{name}: {what}, {reps} reps in {dt:.1f} s")
-    return rates, threads, "; ".join(samples)
+                return reps, dt
+
+    rates, samples = {}, []
+    rs_db = u32(w.rs_sample_db)
+    h_s = u32(w.ep_sample_h)
+    for m, B in ((2, 1), (32, 16)):
+        ct = u32(w.ct[m][:, :, a:b])
+        reps, dt = timed(lambda ct=ct: oracle.rowsel(ct, rs_db, npts, qr, nthreads=threads))
+        rates[f"rowsel_48GiB_B{B}"] = reps * rs_db.nbytes / dt
+        samples.append(f"rowsel_48GiB_B{B}: points {a}..{b - 1} x {RS_D0}x{RS_D1}, m={m}, {reps} reps in {dt:.1f} s")
+    sc_db = fetch(w.sdb[:CPU_SAMPLE_ROWS]).view("int8")
+    for B in (1, 32):
+        Q = u32(w.q[B])
+        reps, dt = timed(lambda Q=Q: oracle.scalar(sc_db, Q, nthreads=threads))
+        rates[f"scalar_64GiB_B{B}"] = reps * sc_db.nbytes / dt
+        samples.append(f"scalar_64GiB_B{B}: rows 0..{CPU_SAMPLE_ROWS - 1} x {SC_K}, B={B}, {reps} reps in {dt:.1f} s")
+    for B in (1, 16):
+        C, G = u32(w.ec[B][:, :, a:b]), u32(w.eg[B][:, :, a:b])
+        reps, dt = timed(lambda C=C, G=G: oracle.exppack(h_s, C, G, npts, qr, nthreads=threads))
+        rates[f"exppack_15GiB_B{B}"] = reps * h_s.nbytes / dt
+        samples.append(f"exppack_15GiB_B{B}: points {a}..{b - 1} x {EP_DR}x{EP_N}, B={B}, {reps} reps in {dt:.1f} s")
+    if hasattr(w, "ncoef"):
+        npolys = threads
+        coef = u32(w.ncoef[:npolys])
+        res = oracle.ntt_rns(coef, RS_Q, NTT_PSI, nthreads=threads)
+        R = len(RS_Q)
+        for name, fn in (("ntt_rns_fwd_hint", lambda: oracle.ntt_rns(coef, RS_Q, NTT_PSI, nthreads=threads)),
+                         ("ntt_inv_hint", lambda: oracle.ntt_batch(res, RS_Q, NTT_PSI, inverse=True, nthreads=threads)),
+                         ("ntt_fwd_hint", lambda: oracle.ntt_batch(res, RS_Q, NTT_PSI, nthreads=threads))):
+            reps, dt = timed(fn)
+            rates[name] = reps * 4 * npolys * R * RS_N / dt
+            samples.append(f"{name}: polynomials 0..{npolys - 1} x {R} limbs x N={RS_N}, {reps} reps in {dt:.1f} s")
+    # one thread, whole configurations: tiny RowSel and scalar 1 GiB
+    single = {}
+    N, m, D0, D1 = 256, 2, 16, 8
+    tq = [1073738753, 1073732609]
+    P = N * len(tq)
+    dev = torch.device("cuda:0")
+    t_ct = torch.empty((m, D0, P), dtype=torch.int32, device=dev)
+    t_db = torch.empty((D0, D1, P), dtype=torch.int32, device=dev)
+    synth.fill_residues_(t_ct, 1, synth.STREAM_ROWSEL_CT, N, tq)
+    synth.fill_residues_(t_db, 1, synth.STREAM_ROWSEL_DB, N, tq)
+    ct, db = u32(t_ct), u32(t_db)
+    reps, dt = timed(lambda: oracle.rowsel(ct, db, N, tq, nthreads=1))
+    single["rowsel_tiny"] = {"GBps": reps * db.nbytes / dt / 1e9, "reps": reps, "s": dt}
+    if getattr(w, "small", None):
+        sdb = fetch(w.small["sdb"]).view("int8")
+        for B in (1, 8):
+            Q = u32(w.small[f"q{B}"])
+            for label, nt in ((f"scalar_1GiB_B{B}", 1), (f"scalar_1GiB_B{B}_all_threads", threads)):
+                t0 = time.perf_counter()
+                oracle.scalar(sdb, Q, nthreads=nt)
+                dt = time.perf_counter() - t0
+                if nt == 1:
+                    single[label] = {"GBps": sdb.nbytes / dt / 1e9, "reps": 1, "s": dt}
+                else:
+                    rates[f"scalar_1GiB_B{B}"] = sdb.nbytes / dt
+        samples.append(f"scalar_1GiB_B1/B8: the whole 1 GiB DB, one pass each on 1 and on {threads} threads")
+    d2h = {"bytes": copies["bytes"], "s": copies["s"],
+           "GBps": copies["bytes"] / copies["s"] / 1e9 if copies["s"] > 0 else None}
+    return rates, host, "; ".join(samples), d2h, single
 
 
 def read_reference(torch, pirscan, bufs, steps, warmup, stream):
@@ -589,6 +793,9 @@ def main():
     ap.add_argument("--skip-shapes", action="store_true",
                     help="leave out the scalar hint / second-fold / D/D0 rows (profiling runs: their MFMA "
                          "launches share one grid size with the step's B=32 scan)")
+    ap.add_argument("--skip-config-rows", action="store_true",
+                    help="leave out the other configurations' rows (profiling runs: the RowSel 3 GiB scan "
+                         "shares a kernel and grid size with ExpPack B=1)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one torch copy of this many GiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -651,6 +858,16 @@ def main():
     next_rows = {name: workload_entry(name, nscans[name], *ntimes[name]) for name in nscans}
 
     nsteps = min(args.steps, 3)
+    config_rows = None
+    if not args.skip_config_rows:
+        log("configuration rows: row-major entry point at 64 GiB, scalar 1 GiB, RowSel 3 GiB")
+        cscans = w.rowmajor_scans()
+        cscans.update(w.small_config_scans())
+        _, ctimes = time_scans(torch, w.pirscan, cscans, args.steps, args.warmup, stream)
+        config_rows = {name: workload_entry(name, cscans[name], *ctimes[name]) for name in cscans}
+        del cscans, w.rm_bufs
+        torch.cuda.empty_cache()
+
     shape_rows = None
     if not args.skip_shapes:
         log("next rows: scalar product at the hint, second-fold and D/D0 shapes")
@@ -667,6 +884,16 @@ def main():
             del tiled, sscans
             torch.cuda.empty_cache()
         shape_rows = {name: shape_rows[name] for name in SHAPE_SCANS}
+
+    if not args.skip_config_rows:
+        log("configuration rows: the 48 GiB RowSel DB on the VALU scan")
+        if hasattr(w, "sdbt"):
+            del w.sdbt  # the step is done: room for the word layout beside the p-major DB
+        vscans = w.valu48_scans()
+        _, vtimes = time_scans(torch, w.pirscan, vscans, nsteps, 1, stream)
+        config_rows.update({name: workload_entry(name, vscans[name], *vtimes[name]) for name in vscans})
+        del vscans, w.vdbt, w.vws
+        torch.cuda.empty_cache()
 
     w.setup_ntt()
     log("next rows: NTT / INTT over the hint's polynomials")
@@ -696,6 +923,16 @@ def main():
         "roofline": dict(per[dominant]["roofline"], kernel=SCAN_KERNELS[dominant], scan=dominant),
         "hbm_read_reference": read_ref,
         "workloads": per,
+        "config_rows": {"config": {"scalar_64GiB_rowmajor": {"M": SC_M, "K": SC_K, "B": [1, 32],
+                                                             "entry_point": "pirscan_scalar_gemm_u32"},
+                                   "scalar_1GiB": {"M": SC_SMALL, "K": SC_SMALL, "B": [1, 8],
+                                                   "entry_points": ["pirscan_scalar_gemm_u32_tiled",
+                                                                    "pirscan_scalar_gemm_u32"]},
+                                   "rowsel_3GiB": {"N": RS_N, "R": len(RS_Q), "D0": RS_MED_D, "D1": RS_MED_D,
+                                                   "m": 2, "scan": ["auto (int8 MFMA)", "valu"]},
+                                   "rowsel_48GiB_valu": {"D0": RS_D0, "D1": RS_D1, "m": [2, 32], "scan": "valu",
+                                                         "steps": nsteps}},
+                        "workloads": config_rows},
         "next_rows": {"exppack": {"config": {"N": RS_N, "R": len(RS_Q), "Dr": EP_DR, "n": EP_N, "B": [1, 16],
                                              "hint_GiB": 4 * RS_N * len(RS_Q) * EP_DR * EP_N / 2**30},
                                   "workloads": next_rows},
@@ -709,12 +946,14 @@ def main():
                               "workloads": ntt_rows}},
     }
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle on bounded samples)")
-        rates, cores, sample = cpu_baseline()
+        log("cpu baseline (the oracle on samples of the device inputs, host cores)")
+        rates, host, sample, d2h, single = cpu_baseline(w)
         t_cpu = sum(scans[n][1] / rates[n] for n in scans)
-        result["cpu_baseline"] = {"value": total_db / t_cpu / 1e9, "unit": "GB/s", "cores": cores,
-                                  "kind": "oracle", "sample": sample,
-                                  "per_scan_GBps": {n: r / 1e9 for n, r in rates.items()}}
+        result["cpu_baseline"] = {"value": total_db / t_cpu / 1e9, "unit": "GB/s", "cores": host["threads_used"],
+                                  "kind": "oracle", "sample": sample, "host": host,
+                                  "per_scan_GBps": {n: r / 1e9 for n, r in rates.items()},
+                                  "gpu_over_oracle_step": value / (total_db / t_cpu / 1e9),
+                                  "d2h_copy": d2h, "single_thread": single}
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
