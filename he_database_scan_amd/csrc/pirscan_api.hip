@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/pirscan.h"
 #include "internal.hpp"
@@ -259,6 +260,39 @@ int run_ntt(const pirscan_ntt_shape* s, pirscan::NttMode mode, const void* plan,
   return device_status(pirscan::launch_ntt(d, mode, plan, in, out, count, (hipStream_t)stream));
 }
 
+// ---- scratch of the no-allocation entry point --------------------------------
+
+// The scratch buffer of pirscan_scalar_gemm_u32_noalloc.  Each GPU the library
+// runs on holds its own copy, at its own address, until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) uint8_t scratch[PIRSCAN_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PIRSCAN_EUNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return device_status(e);
+      if (!p) return PIRSCAN_EDEVICE;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PIRSCAN_OK;
+}
+
 }  // namespace
 
 namespace pirscan {
@@ -434,6 +468,25 @@ int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* o
       pirscan::launch_scalar(db, query, out, M, K, B, p, workspace, (hipStream_t)stream));
 }
 
+int pirscan_scalar_gemm_u32_noalloc(const int8_t* db, const uint32_t* query, uint32_t* out, uint64_t M,
+                                    uint64_t K, uint32_t B, void* stream) {
+  if (!db || !query || !out) return PIRSCAN_EINVAL;
+  pirscan::ScalarPlan p;
+  if (!pirscan::scalar_plan(M, K, B, reinterpret_cast<uintptr_t>(db), &p)) return PIRSCAN_EINVAL;
+  const uint64_t db_bytes = M * K, q_bytes = K * B * 4ull, o_bytes = M * B * 4ull;
+  if (overlap(out, o_bytes, db, db_bytes) || overlap(out, o_bytes, query, q_bytes)) return PIRSCAN_EINVAL;
+  const bool needs_scratch = p.fast && p.total_bytes > 0;
+  if (needs_scratch && p.total_bytes > PIRSCAN_NOALLOC_SCRATCH_BYTES) return PIRSCAN_ESCRATCH;
+  const int dc = device_check();
+  if (dc != PIRSCAN_OK) return dc;
+  void* ws = nullptr;
+  if (needs_scratch) {
+    const int sc = scratch_on_current_device(&ws);
+    if (sc != PIRSCAN_OK) return sc;
+  }
+  return device_status(pirscan::launch_scalar(db, query, out, M, K, B, p, ws, (hipStream_t)stream));
+}
+
 size_t pirscan_scalar_layout_db_bytes(uint64_t M, uint64_t K) {
   pirscan::ScalarPlan p;
   if (!pirscan::scalar_tiled_plan(M, K, 1, &p)) return 0;
@@ -512,6 +565,7 @@ const char* pirscan_strerror(int status) {
     case PIRSCAN_EINVAL: return "invalid argument";
     case PIRSCAN_EDEVICE: return "HIP runtime error";
     case PIRSCAN_EUNSUPPORTED: return "unsupported device (gfx950 required)";
+    case PIRSCAN_ESCRATCH: return "problem needs more than the no-allocation entry point's scratch buffer";
     default: return "unknown status";
   }
 }

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libpirscan.so")
 BENCH_LIB_PATH = os.path.join(_HERE, "libpirscan_bench.so")
 MAX_R = 8
 
-OK, EINVAL, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3
+OK, EINVAL, EDEVICE, EUNSUPPORTED, ESCRATCH = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 72 << 20   # PIRSCAN_NOALLOC_SCRATCH_BYTES
 SCAN_AUTO, SCAN_VALU = 0, 1   # PIRSCAN_SCAN_*: which scan kernel (and stored layout) a shape uses
 
 
@@ -191,6 +192,8 @@ class Library:
             L.pirscan_scalar_workspace_bytes.restype = sz
             L.pirscan_scalar_gemm_u32.argtypes = [vp, vp, vp, u64, u64, u32, vp, sz, vp]
             L.pirscan_scalar_gemm_u32.restype = ctypes.c_int
+            L.pirscan_scalar_gemm_u32_noalloc.argtypes = [vp, vp, vp, u64, u64, u32, vp]
+            L.pirscan_scalar_gemm_u32_noalloc.restype = ctypes.c_int
             L.pirscan_scalar_layout_db_bytes.argtypes = [u64, u64]
             L.pirscan_scalar_layout_db_bytes.restype = sz
             L.pirscan_scalar_layout_db.argtypes = [vp, vp, u64, u64, vp]
@@ -326,6 +329,19 @@ class Library:
                     self._load().pirscan_scalar_gemm_u32(_ptr(db), _ptr(query), _ptr(out), M, K, B,
                                                          _ptr(workspace) if need else ctypes.c_void_p(0),
                                                          _nbytes(workspace), _stream(stream)))
+
+    def scalar_gemm_u32_noalloc(self, db, query, out, stream=None) -> None:
+        """As :meth:`scalar_gemm_u32`, with the library's built-in scratch buffer
+        instead of a workspace: for callers that cannot allocate.  Calls that
+        overlap in time on one GPU share that buffer and race."""
+        M, K = db.shape
+        B = query.shape[1] if query.dim() == 2 else 1
+        _dev(db, "db", 1, M * K)
+        _dev(query, "query", 4, K * B)
+        _dev(out, "out", 4, M * B)
+        self._check("pirscan_scalar_gemm_u32_noalloc",
+                    self._load().pirscan_scalar_gemm_u32_noalloc(_ptr(db), _ptr(query), _ptr(out), M, K, B,
+                                                                 _stream(stream)))
 
     def scalar_layout_db_bytes(self, M: int, K: int) -> int:
         return int(self._load().pirscan_scalar_layout_db_bytes(M, K))
@@ -470,7 +486,8 @@ def _forward(name):
 
 for _name in ("version", "strerror", "layout_db_bytes", "layout_db", "rowsel_workspace_bytes", "rowsel_modgemm",
               "exppack_layout_h_bytes", "exppack_layout_h", "exppack_workspace_bytes", "exppack_modgemm",
-              "scalar_workspace_bytes", "scalar_gemm_u32", "scalar_layout_db_bytes", "scalar_layout_db",
+              "scalar_workspace_bytes", "scalar_gemm_u32", "scalar_gemm_u32_noalloc", "scalar_layout_db_bytes",
+              "scalar_layout_db",
               "scalar_tiled_workspace_bytes", "scalar_gemm_u32_tiled", "ntt_plan_bytes", "ntt_plan_init",
               "ntt_forward", "ntt_inverse", "ntt_rns_forward", "bench_read", "kernel_timer_begin",
               "kernel_timer_end"):

@@ -60,7 +60,10 @@ enum {
                                 range, unknown scan kind, output overlapping an
                                 input, workspace too small, size overflow */
   PIRSCAN_EDEVICE = -2,      /* a HIP call failed; see pirscan_last_device_error */
-  PIRSCAN_EUNSUPPORTED = -3  /* current device is not gfx950 */
+  PIRSCAN_EUNSUPPORTED = -3, /* current device is not gfx950 */
+  PIRSCAN_ESCRATCH = -4      /* the problem needs more scratch memory than the
+                                built-in buffer of the no-allocation entry point
+                                (PIRSCAN_NOALLOC_SCRATCH_BYTES) holds */
 };
 
 /*
@@ -237,6 +240,27 @@ size_t pirscan_scalar_workspace_bytes(uint64_t M, uint64_t K, uint32_t B);
 int pirscan_scalar_gemm_u32(const int8_t* db, const uint32_t* query, uint32_t* out,
                             uint64_t M, uint64_t K, uint32_t B,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pirscan_scalar_gemm_u32 without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the digit planes and split-K
+ * partial sums live in a scratch buffer built into the library, one per GPU,
+ * of PIRSCAN_NOALLOC_SCRATCH_BYTES, which each GPU the library runs on holds
+ * until the process ends.  Same arguments, layouts and result as
+ * pirscan_scalar_gemm_u32; the call allocates nothing.
+ *   Returns PIRSCAN_ESCRATCH when pirscan_scalar_workspace_bytes(M, K, B)
+ *   exceeds PIRSCAN_NOALLOC_SCRATCH_BYTES (every B at M = K = 2^18, the
+ *   64 GiB database, fits), before touching the device.
+ *   Every call on one GPU shares that GPU's buffer: calls that overlap in
+ *   time on one GPU (on different streams, or from different threads without
+ *   ordering between their streams) race and give undefined results.  Calls
+ *   ordered on one stream are safe; nothing in the buffer has to start at any
+ *   particular value.
+ */
+#define PIRSCAN_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+int pirscan_scalar_gemm_u32_noalloc(const int8_t* db, const uint32_t* query, uint32_t* out,
+                                    uint64_t M, uint64_t K, uint32_t B, void* stream);
 
 /*
  * Tiled scalar database.  The DB is static (VIPIR section 2.5: the server

@@ -383,3 +383,18 @@ def test_ntt_rejects_bad_arguments_without_a_device():
     assert L.pirscan_ntt_plan_init(ctypes.byref(s), ctypes.c_void_p(PL), 16 * 3 * 4096 - 1, None) == \
         pirscan.EINVAL                                     # short plan
     assert L.pirscan_ntt_plan_init(ctypes.byref(s), ctypes.c_void_p(0), 1 << 20, None) == pirscan.EINVAL
+
+
+def test_noalloc_entry_point_limits_without_a_device():
+    """The no-allocation scalar product refuses, before touching a device,
+    problems whose scratch exceeds its built-in buffer, and bad arguments."""
+    L = pirscan.lib()
+    vp = ctypes.c_void_p
+    A, Q, O = vp(1 << 40), vp(1 << 44), vp(1 << 45)   # never dereferenced
+    f = L.pirscan_scalar_gemm_u32_noalloc
+    assert pirscan.scalar_workspace_bytes(1 << 19, 1 << 18, 1) > pirscan.NOALLOC_SCRATCH_BYTES
+    assert f(A, Q, O, 1 << 19, 1 << 18, 1, None) == pirscan.ESCRATCH
+    assert f(None, Q, O, 64, 4096, 1, None) == pirscan.EINVAL
+    assert f(A, Q, O, 0, 4096, 1, None) == pirscan.EINVAL
+    assert f(A, Q, vp((1 << 40) + 8), 64, 4096, 1, None) == pirscan.EINVAL   # out overlaps db
+    assert "scratch" in pirscan.strerror(pirscan.ESCRATCH)
