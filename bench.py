@@ -136,6 +136,20 @@ KERNEL_SOURCES = {
 }
 
 
+def selected(spec: str, names, skip: bool) -> set:
+    """The row names a comma-separated --shapes / --config-rows value picks
+    (all, none, or names), empty when the matching --skip flag is set."""
+    if skip or spec == "none":
+        return set()
+    if spec == "all":
+        return set(names)
+    want = {n for n in spec.split(",") if n}
+    unknown = want - set(names)
+    if unknown:
+        raise SystemExit(f"unknown rows: {sorted(unknown)}")
+    return want
+
+
 def code_text(text: str) -> str:
     """A kernel source without its comments and blank lines: what the counters
     depend on (a comment edit keeps the profiled traffic valid)."""
@@ -566,6 +580,72 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_gib: float) -> d
     return out
 
 
+# MI355X unit counts for the counter-derived rates
+SIMDS = 256 * 4
+MFMA_INT8_OPS_PER_SIMD_CLK = MFMA_INT8_PEAK_TOPS * 1e12 / (SIMDS * 2.4e9)  # 2035: the published peak at 2.4 GHz
+COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+            "SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def counters_from(csv_paths) -> dict:
+    """Per-scan figures from rocprofv3 --pmc collections of this benchmark
+    (counters COUNTERS, summed over the chip's instances by rocprofv3):
+    the dispatch's duration; GRBM_GUI_ACTIVE per XCD (the kernel's GPU clock
+    cycles) and the achieved clock it implies; the MFMA busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles); the VALU busy fraction
+    (SQ_ACTIVE_INST_VALU, in quad-cycles, over SIMD cycles); VALU and MFMA
+    instructions issued; the counted int8 MFMA operations (512 per
+    SQ_INSTS_VALU_MFMA_MOPS_I8) against the published peak and against the
+    peak at the achieved clock.  Medians over each scan's dispatches."""
+    import csv
+    import statistics
+
+    disp = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"kernel": _short_kernel_name(r["Kernel_Name"]),
+                                                      "grid": int(r["Grid_Size"]), "c": {}})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    groups, first = {}, {}
+    for did, d in disp.items():
+        g = (d["kernel"], d["grid"])
+        groups.setdefault(g, []).append(d)
+        first[g] = min(first.get(g, 1 << 62), did)
+    out = {}
+    for scan, g in assign_scan_groups(first).items():
+        rows = []
+        for d in groups[g]:
+            c, ns = d["c"], d["ns"]
+            gui = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0  # summed over the 8 XCDs
+            if gui <= 0 or ns <= 0:
+                continue
+            simd_cycles = gui * SIMDS
+            mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0.0) * 512
+            rows.append({"ms": ns / 1e6, "gui_active_cycles": gui, "clock_GHz": gui / ns,
+                         "mfma_busy": c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / simd_cycles,
+                         "valu_busy": 4 * c.get("SQ_ACTIVE_INST_VALU", 0.0) / simd_cycles,
+                         "valu_insts": c.get("SQ_INSTS_VALU", 0.0), "mfma_insts": c.get("SQ_INSTS_MFMA", 0.0),
+                         "int8_ops": mops, "int8_TOPS": mops / ns / 1e3,
+                         "int8_frac_published": mops / ns / 1e3 / MFMA_INT8_PEAK_TOPS,
+                         "int8_frac_at_clock": mops / (simd_cycles * MFMA_INT8_OPS_PER_SIMD_CLK)})
+        if rows:
+            med = {k: statistics.median(r[k] for r in rows) for k in rows[0]}
+            out[scan] = dict(med, kernel=g[0], grid_size=g[1], dispatches=len(rows))
+    return out
+
+
+def counters_markdown(res: dict) -> str:
+    lines = ["| scan | main kernel | dispatches | ms | GUI cycles (per XCD) | clock GHz | MFMA busy | VALU busy | "
+             "int8 TOP/s (counted) | of 5.0 POP/s | of peak at clock |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for scan, r in res.items():
+        lines.append(f"| {scan} | `{r['kernel']}` | {r['dispatches']} | {r['ms']:.3f} | {r['gui_active_cycles']:.3e} | "
+                     f"{r['clock_GHz']:.2f} | {r['mfma_busy']:.3f} | {r['valu_busy']:.3f} | {r['int8_TOPS']:.0f} | "
+                     f"{r['int8_frac_published']:.3f} | {r['int8_frac_at_clock']:.3f} |")
+    return "\n".join(lines)
+
+
 def summarize_trace(trace_csv: str) -> str:
     """Markdown table of a rocprofv3 --kernel-trace CSV of this benchmark:
     launches grouped by (kernel, grid size), with the scan each main-kernel
@@ -793,6 +873,10 @@ def main():
     ap.add_argument("--skip-shapes", action="store_true",
                     help="leave out the scalar hint / second-fold / D/D0 rows (profiling runs: their MFMA "
                          "launches share one grid size with the step's B=32 scan)")
+    ap.add_argument("--shapes", default="all",
+                    help="comma-separated scalar shape rows to run (all, none, or names of SHAPE_SCANS)")
+    ap.add_argument("--config-rows", default="all",
+                    help="comma-separated configuration rows to run (all, none, or names of CONFIG_SCANS)")
     ap.add_argument("--skip-config-rows", action="store_true",
                     help="leave out the other configurations' rows (profiling runs: the RowSel 3 GiB scan "
                          "shares a kernel and grid size with ExpPack B=1)")
@@ -801,11 +885,19 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc counter "
                          "collections (FETCH_SIZE, WRITE_SIZE) of this benchmark")
+    ap.add_argument("--counters-from", nargs="+", metavar="PMC_CSV",
+                    help="no GPU: write profiles/counters.json (and print a markdown table) from rocprofv3 --pmc "
+                         "collections of this benchmark with the counters " + " ".join(COUNTERS))
     ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
                     help="no GPU: print a markdown table of a rocprofv3 --kernel-trace CSV of this benchmark")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return
+    if args.counters_from:
+        res = counters_from(args.counters_from)
+        json.dump(res, open(os.path.join(ROOT, "profiles", "counters.json"), "w"), indent=1)
+        print(counters_markdown(res))
         return
     if args.traffic_from:
         res = traffic_from_counters(*args.traffic_from, calib_gib=args.calib_copy_gib or 4.0)
@@ -858,39 +950,44 @@ def main():
     next_rows = {name: workload_entry(name, nscans[name], *ntimes[name]) for name in nscans}
 
     nsteps = min(args.steps, 3)
+    want_cfg = selected(args.config_rows, CONFIG_SCANS, args.skip_config_rows)
+    want_shapes = selected(args.shapes, SHAPE_SCANS, args.skip_shapes)
     config_rows = None
-    if not args.skip_config_rows:
+    if want_cfg - {"rowsel_48GiB_B1_valu", "rowsel_48GiB_B16_valu"}:
         log("configuration rows: row-major entry point at 64 GiB, scalar 1 GiB, RowSel 3 GiB")
         cscans = w.rowmajor_scans()
         cscans.update(w.small_config_scans())
+        cscans = {name: v for name, v in cscans.items() if name in want_cfg}
         _, ctimes = time_scans(torch, w.pirscan, cscans, args.steps, args.warmup, stream)
         config_rows = {name: workload_entry(name, cscans[name], *ctimes[name]) for name in cscans}
         del cscans, w.rm_bufs
         torch.cuda.empty_cache()
 
     shape_rows = None
-    if not args.skip_shapes:
+    if want_shapes:
         log("next rows: scalar product at the hint, second-fold and D/D0 shapes")
         del w.sdbt  # the step's tiled DB; each [M][K] view below is tiled in turn
         torch.cuda.empty_cache()
         shape_rows = {}
         views = {}
         for name, (M, K, B) in SHAPE_SCANS.items():
-            views.setdefault((M, K), []).append(name)
+            if name in want_shapes:
+                views.setdefault((M, K), []).append(name)
         for (M, K), names in views.items():
             tiled, sscans = w.shape_scans(M, K, names)
             _, stimes = time_scans(torch, w.pirscan, sscans, nsteps, 1, stream)
             shape_rows.update({name: workload_entry(name, sscans[name], *stimes[name]) for name in sscans})
             del tiled, sscans
             torch.cuda.empty_cache()
-        shape_rows = {name: shape_rows[name] for name in SHAPE_SCANS}
+        shape_rows = {name: shape_rows[name] for name in SHAPE_SCANS if name in shape_rows}
 
-    if not args.skip_config_rows:
+    if want_cfg & {"rowsel_48GiB_B1_valu", "rowsel_48GiB_B16_valu"}:
         log("configuration rows: the 48 GiB RowSel DB on the VALU scan")
         if hasattr(w, "sdbt"):
             del w.sdbt  # the step is done: room for the word layout beside the p-major DB
-        vscans = w.valu48_scans()
+        vscans = {name: v for name, v in w.valu48_scans().items() if name in want_cfg}
         _, vtimes = time_scans(torch, w.pirscan, vscans, nsteps, 1, stream)
+        config_rows = config_rows or {}
         config_rows.update({name: workload_entry(name, vscans[name], *vtimes[name]) for name in vscans})
         del vscans, w.vdbt, w.vws
         torch.cuda.empty_cache()
