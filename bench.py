@@ -521,12 +521,19 @@ SCAN_KERNELS = {
 }
 
 
+# the scans the current run launches (all of SCAN_KERNELS unless row filters
+# leave some out), in launch order: profile summaries attribute kernel groups
+# to these only
+RUN_SCANS = list(SCAN_KERNELS)
+
+
 def assign_scan_groups(groups):
     """groups: {(kernel, grid): first dispatch id}.  Returns {scan: (kernel,
-    grid)}, giving each scan, in SCAN_KERNELS order, the earliest group of its
-    kernel not yet taken."""
+    grid)}, giving each scan of the run, in launch order, the earliest group of
+    its kernel not yet taken."""
     taken, out = set(), {}
-    for scan, pat in SCAN_KERNELS.items():
+    for scan in RUN_SCANS:
+        pat = SCAN_KERNELS[scan]
         cands = sorted((first, g) for g, first in groups.items() if g[0].startswith(pat) and g not in taken)
         if cands:
             out[scan] = cands[0][1]
@@ -888,16 +895,23 @@ def main():
     ap.add_argument("--counters-from", nargs="+", metavar="PMC_CSV",
                     help="no GPU: write profiles/counters.json (and print a markdown table) from rocprofv3 --pmc "
                          "collections of this benchmark with the counters " + " ".join(COUNTERS))
+    ap.add_argument("--counters-out", default=os.path.join(ROOT, "profiles", "counters.json"),
+                    help="where --counters-from writes its JSON")
     ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
                     help="no GPU: print a markdown table of a rocprofv3 --kernel-trace CSV of this benchmark")
     args = ap.parse_args()
-    if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace))
-        return
+    # the scans this run (or the run a profile summary below describes) launches
+    want_cfg = selected(args.config_rows, CONFIG_SCANS, args.skip_config_rows)
+    want_shapes = selected(args.shapes, SHAPE_SCANS, args.skip_shapes)
+    RUN_SCANS[:] = [n for n in SCAN_KERNELS
+                    if (n not in CONFIG_SCANS or n in want_cfg) and (n not in SHAPE_SCANS or n in want_shapes)]
     if args.counters_from:
         res = counters_from(args.counters_from)
-        json.dump(res, open(os.path.join(ROOT, "profiles", "counters.json"), "w"), indent=1)
+        json.dump(res, open(args.counters_out, "w"), indent=1)
         print(counters_markdown(res))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
         return
     if args.traffic_from:
         res = traffic_from_counters(*args.traffic_from, calib_gib=args.calib_copy_gib or 4.0)
@@ -950,8 +964,6 @@ def main():
     next_rows = {name: workload_entry(name, nscans[name], *ntimes[name]) for name in nscans}
 
     nsteps = min(args.steps, 3)
-    want_cfg = selected(args.config_rows, CONFIG_SCANS, args.skip_config_rows)
-    want_shapes = selected(args.shapes, SHAPE_SCANS, args.skip_shapes)
     config_rows = None
     if want_cfg - {"rowsel_48GiB_B1_valu", "rowsel_48GiB_B16_valu"}:
         log("configuration rows: row-major entry point at 64 GiB, scalar 1 GiB, RowSel 3 GiB")
