@@ -2,6 +2,7 @@
 // check, constant precomputation and kernel dispatch on the caller's stream.
 // Every entry point declared in include/pirscan.h is defined here.
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -176,6 +177,11 @@ int run_modgemm(const pirscan::RowselLaunch& a, uint32_t R, const Span* bufs, in
   return device_status(pirscan::launch_rowsel(a, workspace, (hipStream_t)stream));
 }
 
+// Optional input validation (defined below, with its device flag).
+bool validation_on();
+int check_residues(const uint32_t* x, uint64_t words, uint64_t P, uint32_t N, const uint32_t* q, uint32_t R,
+                   hipStream_t stream);
+
 // ---- NTT shape validation (host) -----------------------------------------
 
 uint32_t host_mulmod(uint32_t a, uint32_t b, uint32_t q) { return (uint32_t)(((uint64_t)a * b) % q); }
@@ -257,7 +263,76 @@ int run_ntt(const pirscan_ntt_shape* s, pirscan::NttMode mode, const void* plan,
   if (overlap(plan, plan_b, out, (uint64_t)ow * 4)) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
+  if (mode != pirscan::NttMode::kRnsForward && validation_on()) {
+    const int vc = check_residues(in, (uint64_t)ow, (uint64_t)d.R * d.N, d.N, d.q, d.R, (hipStream_t)stream);
+    if (vc != PIRSCAN_OK) return vc;
+  }
   return device_status(pirscan::launch_ntt(d, mode, plan, in, out, count, (hipStream_t)stream));
+}
+
+// ---- optional input validation -------------------------------------------------
+//
+// With PIRSCAN_VALIDATE_INPUTS=1 in the environment (read at every call), the
+// entry points whose inputs are residues check every one against its modulus
+// before any other device work and return PIRSCAN_EINVAL if one is not below
+// it.  A debugging aid: the check synchronises the caller's stream.
+
+bool validation_on() {
+  const char* v = getenv("PIRSCAN_VALIDATE_INPUTS");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+struct Moduli {
+  uint32_t v[PIRSCAN_MAX_R];
+};
+
+// Set to 1 by the check kernel when a word is out of range; one per device.
+__device__ uint32_t g_bad_input;
+std::atomic<void*> g_bad_input_ptr[kMaxDevices];
+
+__global__ void clear_word_kernel(uint32_t* w) {
+  if (threadIdx.x == 0) *w = 0;
+}
+
+// Word i of an array whose last axis is the P = R*N points belongs to limb
+// (i % P) / N.
+__global__ __launch_bounds__(256) void check_residues_kernel(const uint32_t* __restrict__ x, uint64_t words,
+                                                             uint64_t P, uint32_t N, Moduli q,
+                                                             uint32_t* __restrict__ bad) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  bool any = false;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += stride)
+    any |= x[i] >= q.v[(i % P) / N];
+  if (any) *bad = 1;
+}
+
+// Checks words < q[(i % P) / N] for every word of x; PIRSCAN_EINVAL if one is not.
+int check_residues(const uint32_t* x, uint64_t words, uint64_t P, uint32_t N, const uint32_t* q, uint32_t R,
+                   hipStream_t stream) {
+  if (!x || words == 0) return PIRSCAN_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PIRSCAN_EUNSUPPORTED;
+  void* flag = g_bad_input_ptr[dev].load(std::memory_order_acquire);
+  if (!flag) {
+    e = hipGetSymbolAddress(&flag, HIP_SYMBOL(g_bad_input));
+    if (e != hipSuccess) return device_status(e);
+    g_bad_input_ptr[dev].store(flag, std::memory_order_release);
+  }
+  Moduli m{};
+  for (uint32_t r = 0; r < R && r < PIRSCAN_MAX_R; ++r) m.v[r] = q[r];
+  uint32_t* f = static_cast<uint32_t*>(flag);
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, f);
+  uint64_t grid = (words + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(check_residues_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, x, words, P, N, m, f);
+  uint32_t host = 0;
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, f, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return device_status(e);
+  return host ? PIRSCAN_EINVAL : PIRSCAN_OK;
 }
 
 // ---- scratch of the no-allocation entry point --------------------------------
@@ -320,6 +395,10 @@ int pirscan_layout_db(const pirscan_rowsel_shape* s, const uint32_t* db_pmajor, 
   if (packed && (reinterpret_cast<uintptr_t>(db_tiled) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
+  if (validation_on()) {
+    const int vc = check_residues(db_pmajor, words, P, s->N, s->q, s->R, (hipStream_t)stream);
+    if (vc != PIRSCAN_OK) return vc;
+  }
   if (packed)  // [D0][D1][P]: column n is fragment row n (stride P), k has stride D1*P
     return device_status(pirscan::launch_pack_operand(db_pmajor, db_tiled, P, s->N, s->q, s->R, s->D1, s->D0, P,
                                                       (uint64_t)s->D1 * P, (hipStream_t)stream));
@@ -375,6 +454,12 @@ int pirscan_rowsel_modgemm(const pirscan_rowsel_shape* s, uint32_t m, const uint
   const uint64_t db_bytes = operand_layout_bytes(s->q, s->R, a.P, s->D0, s->D1, s->scan);
   if (overlap(out, ow * 4, ct, ctw * 4) || overlap(out, ow * 4, db_tiled, db_bytes)) return PIRSCAN_EINVAL;
   const Span ins[] = {{ct, ctw * 4}, {db_tiled, db_bytes}, {out, ow * 4}};
+  if (validation_on()) {
+    const int dc = device_check();
+    if (dc != PIRSCAN_OK) return dc;
+    const int vc = check_residues(ct, ctw, a.P, s->N, s->q, s->R, (hipStream_t)stream);
+    if (vc != PIRSCAN_OK) return vc;
+  }
   return run_modgemm(a, s->R, ins, 3, workspace, workspace_bytes, stream);
 }
 
@@ -394,6 +479,10 @@ int pirscan_exppack_layout_h(const pirscan_exppack_shape* s, const uint32_t* h_p
   if (packed && (reinterpret_cast<uintptr_t>(h_tiled) % 16) != 0) return PIRSCAN_EINVAL;
   const int dc = device_check();
   if (dc != PIRSCAN_OK) return dc;
+  if (validation_on()) {
+    const int vc = check_residues(h_pmajor, h, P, s->N, s->q, s->R, (hipStream_t)stream);
+    if (vc != PIRSCAN_OK) return vc;
+  }
   // The GEMM's DB operand is H^T: hint column i is the reduction index k and
   // row r the output column.  H [Dr][n][P]: r has stride n*P, i stride P.
   if (packed)
@@ -434,6 +523,13 @@ int pirscan_exppack_modgemm(const pirscan_exppack_shape* s, uint32_t B, const ui
   pirscan::RowselLaunch a;
   exppack_launch_desc(s, B, P, C, h_tiled, G, out, &a);
   const Span ins[] = {{C, cw * 4}, {h_tiled, hb}, {G, gb}, {out, ow * 4}};
+  if (validation_on()) {
+    const int dc = device_check();
+    if (dc != PIRSCAN_OK) return dc;
+    int vc = check_residues(C, cw, P, s->N, s->q, s->R, (hipStream_t)stream);
+    if (vc == PIRSCAN_OK && G) vc = check_residues(G, gw, P, s->N, s->q, s->R, (hipStream_t)stream);
+    if (vc != PIRSCAN_OK) return vc;
+  }
   return run_modgemm(a, s->R, ins, 4, workspace, workspace_bytes, stream);
 }
 

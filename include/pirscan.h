@@ -39,6 +39,12 @@
  *    calls).
  *  - All arithmetic is integer; results are exact (bit-identical to the
  *    definitions above).
+ *  - Inputs that are residues (RowSel / ExpPack operands, NTT inputs) must be
+ *    below their modulus; this is not checked on the hot path.  With the
+ *    environment variable PIRSCAN_VALIDATE_INPUTS=1 (read at each call) the
+ *    entry points that take such inputs first check every one on the device
+ *    and return PIRSCAN_EINVAL if one is out of range -- a debugging aid
+ *    that synchronises the caller's stream.
  */
 #ifndef PIRSCAN_H
 #define PIRSCAN_H
