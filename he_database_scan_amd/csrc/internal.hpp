@@ -126,6 +126,7 @@ uint32_t rowsel_fold_period(uint32_t q);
 struct ScalarPlan {
   bool fast;          // aligned fast paths (K % 16 == 0, 16-byte aligned db)
   bool mfma;          // B > 1 on int8 MFMA
+  bool wide;          // passes of 128 columns while more than 64 remain (tiled DB)
   uint32_t bgroup;    // columns per MFMA pass (<= 64)
   uint32_t bpad;      // bgroup rounded up to 16
   uint64_t kblock;    // split-K block (k per partial sum)

@@ -214,6 +214,42 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const uint32_t* __
   }
 }
 
+// S1, wide-pass layout: the same digits in MFMA B-fragment order, one 1 KiB
+// fragment per (64-k step s, plane j, 16-column tile ct): lane (li, lg) holds
+// digit j of query[64s + 16lg + 0..15][col0 + 16ct + li], at 16-byte index
+// ((s * 4 + j) * (bpad / 16) + ct) * 64 + 16 lg + li.  Zero past K and bgroup.
+__global__ __launch_bounds__(kThreads) void split_wide_kernel(const uint32_t* __restrict__ query,
+                                                              uint4* __restrict__ dig, uint64_t K,
+                                                              uint64_t k16_groups, uint32_t bpad, uint32_t bgroup,
+                                                              uint32_t ldq, uint32_t col0) {
+  const uint64_t total = k16_groups * bpad;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  const uint32_t ctiles = bpad / 16;
+  for (uint64_t e = (uint64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const uint64_t g = e / bpad;
+    const uint32_t b = (uint32_t)(e % bpad);
+    uint32_t plane[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) plane[j][w] = 0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint64_t k = g * 16 + t;
+      const uint32_t d = (k < K && b < bgroup) ? signed_digits_word(query[k * ldq + col0 + b]) : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) plane[j][t / 4] |= ((d >> (8 * j)) & 0xFFu) << (8 * (t % 4));
+    }
+    const uint64_t s = g / 4, lg = g % 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 o;
+      o.x = plane[j][0]; o.y = plane[j][1]; o.z = plane[j][2]; o.w = plane[j][3];
+      dig[((s * 4 + j) * ctiles + b / 16) * 64 + lg * 16 + b % 16] = o;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // S3: int8 MFMA GEMM.  A tile = 8 wavefronts x kMfmaRowTiles2*16 rows of one
 // k-block; NT = 16-column tiles = 4 * bpad / 16.  The kernel is persistent:
@@ -463,6 +499,149 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(const int8_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// S3, wide passes (more than 64 query columns, tiled DB): passes of 128 query
+// columns, so a batch of n columns streams the DB ceil(n / 128) times instead
+// of ceil(n / 64).  A tile = 128 rows (8 row tiles, half a tile group of the
+// tiled layout) x 512 digit columns (4 planes x 128 columns) of one k-block,
+// 8 wavefronts: wave w accumulates all 8 row tiles against planes 0..3 of
+// query columns 16w..16w+15 (one column tile per plane), 32 accumulator tiles.
+//  * DB fragments (the A operand, used by all 8 waves) come into a six-step
+//    LDS ring once per workgroup with direct global-to-LDS loads, one 1 KiB
+//    fragment per wave per step, four steps ahead.
+//  * Digit fragments (the B operand, 1 KiB each in fragment order, each used
+//    by one wave) stream from global memory straight into a three-step
+//    register ring, two steps ahead (all workgroups of an XCD walk k together,
+//    so they come from L2).
+// Persistent over tiles like mfma_kernel, with the same XCD-local ranges.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = 8;
+constexpr uint32_t kWideCols = 128;            // query columns per wide pass (= bpad)
+constexpr int kWideRowTiles = 8;               // row tiles per wave (all of the tile's)
+constexpr int kWidePlanes = 4;                 // column tiles per wave: one per digit plane
+constexpr uint64_t kWideRows = kWideRowTiles * 16;  // rows per tile: 128
+constexpr int kWideARing = 6;                  // A ring depth (LDS) in 64-k steps: loads 4 steps ahead
+constexpr int kWideBRing = 3;                  // B ring depth (registers): loads 2 steps ahead
+
+__device__ __forceinline__ void wide_tile(const v4i* __restrict__ dbp, const v4i* dig, uint32_t* __restrict__ dst,
+                                          uint64_t M, uint64_t kblock, uint64_t nkb, uint32_t bgroup, uint64_t ldd,
+                                          uint32_t dcol0, uint64_t kb, uint64_t rb, uint64_t psteps,
+                                          v4i (*aring)[kWideWaves * 64]) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t li = lane % 16, lg = lane / 16;
+  const uint64_t s_first = kb * kblock / 64;  // first 64-k step of this k-block
+  const uint32_t nsteps = (uint32_t)(kblock / 64);
+  // this workgroup's 8 row tiles: tiles 8rb .. 8rb+7, inside tile group rb / 2
+  const uint64_t t0 = rb * 8;
+  const v4i* abase = dbp + ((t0 / kScalarGroupTiles) * psteps * kScalarGroupTiles + t0 % kScalarGroupTiles + wave) * 64 +
+                     lane;
+  // digits in B-fragment order (split_wide_kernel): fragment (step, plane j,
+  // column tile w) is 1 KiB of contiguous lanes
+  constexpr uint32_t kCt = kWideCols / 16;
+  const v4i* bbase = dig + (uint64_t)wave * 64 + lane;
+
+  v4i acc[kWideRowTiles][kWidePlanes];
+#pragma unroll
+  for (int rt = 0; rt < kWideRowTiles; ++rt)
+#pragma unroll
+    for (int j = 0; j < kWidePlanes; ++j) acc[rt][j] = v4i{0, 0, 0, 0};
+
+  // step s's DB fragments -> LDS ring slot s % 3; wave w moves fragment w.
+  // Past the DB's last step the last one is read again: it meets zero digits.
+  auto issue_a = [&](uint32_t s) {
+    uint64_t sg = s_first + s;
+    sg = sg < psteps ? sg : psteps - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(abase + sg * (64 * kScalarGroupTiles)),
+                                     LDS_PTR(aring[s % kWideARing] + wave * 64), 16, 0, 0);
+  };
+  v4i bb[kWideBRing][kWidePlanes];
+  auto load_b = [&](int slot, uint32_t s) {
+    const uint32_t ss = s < nsteps ? s : nsteps - 1;  // past the end: a harmless reload
+    const v4i* bs = bbase + (s_first + ss) * (4ull * kCt * 64);
+#pragma unroll
+    for (int j = 0; j < kWidePlanes; ++j) bb[slot][j] = bs[j * kCt * 64];
+  };
+  // One step.  Per step B(s+2) (4 loads), then A(s+4) (1) are issued.  At
+  // the wait of step s the loads issued after B(s) are A(s+2), B(s+1) and
+  // A(s+3), six in all, so vmcnt(6) leaves A(s) (issued before B(s)) and B(s)
+  // landed.  The barrier publishes every wave's share of A(s) and tells each
+  // wave that all others are done with step s-2's slot, which A(s+4)
+  // overwrites; B(s+2) goes to register slot (s+2) % 3, last read by step
+  // s-1's MFMAs.
+  auto step = [&](auto slot_tag, uint32_t s) {
+    constexpr int slot = decltype(slot_tag)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kWidePlanes + 2));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const v4i* as = aring[s % kWideARing] + lane;
+    v4i af[kWideRowTiles];
+#pragma unroll
+    for (int rt = 0; rt < kWideRowTiles; ++rt) af[rt] = as[rt * 64];
+    __builtin_amdgcn_sched_barrier(0);
+    load_b((slot + 2) % kWideBRing, s + 2);
+    issue_a(s + 4);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rt = 0; rt < kWideRowTiles; ++rt)
+#pragma unroll
+      for (int j = 0; j < kWidePlanes; ++j)
+        acc[rt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[rt], bb[slot][j], acc[rt][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  issue_a(0);
+  issue_a(1);
+  load_b(0, 0);
+  issue_a(2);
+  load_b(1, 1);
+  issue_a(3);
+  uint32_t s = 0;
+  for (; s + 2 < nsteps; s += 3) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    step(std::integral_constant<int, 2>{}, s + 2);
+  }
+  if (s < nsteps) step(std::integral_constant<int, 0>{}, s);
+  if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
+  __builtin_amdgcn_s_waitcnt(0);  // no ring load may outlive this tile's use of the LDS
+  __syncthreads();                // the next tile's prologue overwrites the ring
+
+  // D element i of lane l is (row 4*(l/16) + i, column l%16) of a tile;
+  // this wave's column tile j is plane j of query columns 16w + 0..15
+  const uint32_t b = 16 * wave + li;
+  if (b >= bgroup) return;
+#pragma unroll
+  for (int rt = 0; rt < kWideRowTiles; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t row = rb * kWideRows + rt * 16 + 4 * lg + i;
+      if (row >= M) continue;
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < kWidePlanes; ++j) v += (uint32_t)acc[rt][j][i] << (8 * j);
+      if (nkb == 1) dst[row * ldd + dcol0 + b] = v;
+      else dst[(kb * M + row) * bgroup + b] = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * kWideWaves) void mfma_wide_kernel(const v4i* __restrict__ dbp, const v4i* dig,
+                                                                     uint32_t* __restrict__ dst, uint64_t M,
+                                                                     uint64_t kblock, uint64_t nkb,
+                                                                     uint64_t row_blocks, uint32_t bgroup,
+                                                                     uint64_t ldd, uint32_t dcol0, uint64_t psteps) {
+  __shared__ v4i aring[kWideARing][kWideWaves * 64];
+  constexpr uint32_t kXcds = 8;
+  const uint32_t hw = blockIdx.x, G = gridDim.x;  // G >= kXcds (host guarantees)
+  const uint32_t xcd = hw % kXcds, j = hw / kXcds;
+  const uint32_t per_xcd = (G - xcd + kXcds - 1) / kXcds;
+  const uint64_t tiles = nkb * row_blocks;
+  const uint64_t lo = tiles * xcd / kXcds, hi = tiles * (xcd + 1) / kXcds;
+  for (uint64_t t = lo + j; t < hi; t += per_xcd)
+    wide_tile(dbp, dig, dst, M, kblock, nkb, bgroup, ldd, dcol0, t / row_blocks, t % row_blocks, psteps, aring);
+}
+
+// ---------------------------------------------------------------------------
 // Split-K reduction: out[row*ldo + col0 + b] = sum_kb part[(kb*M + row)*cols + b]
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const uint32_t* __restrict__ part,
@@ -507,9 +686,9 @@ uint32_t grid_for(uint64_t items, uint64_t cap = 1u << 20) {
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 uint64_t align_up(uint64_t a, uint64_t b) { return ceil_div(a, b) * b; }
 
-// Workgroups of mfma_kernel<NT, PACKED> the current device holds at once
-// (compute units x occupancy), queried once per device and kept.
-template <int NT, bool PACKED>
+// Workgroups of kernel KERNEL (THREADS threads each) the current device
+// holds at once (compute units x occupancy), queried once per device and kept.
+template <auto KERNEL, int THREADS>
 hipError_t resident_workgroups(uint64_t* out) {
   static std::atomic<uint64_t> cache[kMaxDevices];  // 0: not yet queried
   int dev = 0, cus = 0, per_cu = 0;
@@ -524,8 +703,7 @@ hipError_t resident_workgroups(uint64_t* out) {
     }
   }
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<NT, PACKED>, 64 * kMfmaWaves, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERNEL, THREADS, 0);
   if (e != hipSuccess) return e;
   const uint64_t v = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)(per_cu > 0 ? per_cu : 1);
   if (cached) cache[dev].store(v, std::memory_order_relaxed);
@@ -542,13 +720,29 @@ hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint
   if (pl.kblock % kMfmaChunkK != 0) return hipErrorInvalidValue;
   // persistent: as many workgroups as are co-resident, at least one per XCD
   uint64_t grid = 0;
-  const hipError_t e = resident_workgroups<NT, PACKED>(&grid);
+  const hipError_t e = resident_workgroups<mfma_kernel<NT, PACKED>, 64 * kMfmaWaves>(&grid);
   if (e != hipSuccess) return e;
   if (grid > row_blocks * pl.nkb) grid = row_blocks * pl.nkb;
   if (grid < 8) grid = 8;
   hipLaunchKernelGGL((mfma_kernel<NT, PACKED>), dim3((uint32_t)grid), dim3(64 * kMfmaWaves), 0, stream, db,
                      dig, dst, M, K, pl.kblock, pl.nkb, row_blocks, bgroup, ldd, dcol0,
                      ceil_div(M, 16 * kScalarGroupTiles) * kScalarGroupTiles, ceil_div(K, 64));
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_wide(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint64_t M, uint64_t K,
+                            const ScalarPlan& pl, uint32_t bgroup, uint64_t ldd, uint32_t dcol0,
+                            hipStream_t stream) {
+  const uint64_t row_blocks = ceil_div(M, kWideRows);
+  if (pl.kblock % 64 != 0) return hipErrorInvalidValue;
+  uint64_t grid = 0;
+  const hipError_t e = resident_workgroups<mfma_wide_kernel, 64 * kWideWaves>(&grid);
+  if (e != hipSuccess) return e;
+  if (grid > row_blocks * pl.nkb) grid = row_blocks * pl.nkb;
+  if (grid < 8) grid = 8;
+  hipLaunchKernelGGL(mfma_wide_kernel, dim3((uint32_t)grid), dim3(64 * kWideWaves), 0, stream,
+                     reinterpret_cast<const v4i*>(db), reinterpret_cast<const v4i*>(dig), dst, M, pl.kblock, pl.nkb,
+                     row_blocks, bgroup, ldd, dcol0, ceil_div(K, 64));
   return hipGetLastError();
 }
 
@@ -662,29 +856,42 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const u32x4* __res
   }
 }
 
-// The MFMA passes of up to kMfmaMaxCols query columns: digit split, scan,
-// split-K reduction.
+// The MFMA passes: digit split, scan, split-K reduction.  Passes take up to
+// kMfmaMaxCols query columns, or kWideCols on the tiled DB while more than
+// kMfmaMaxCols columns remain (the plan's `wide`).
 template <bool PACKED>
 hipError_t run_mfma_passes(const int8_t* db, const uint32_t* query, uint32_t* out, uint64_t M, uint64_t K,
                            uint32_t B, const ScalarPlan& pl, uint8_t* dig, uint32_t* part, hipStream_t stream) {
   hipError_t e;
-  for (uint32_t c0 = 0; c0 < B; c0 += pl.bgroup) {
-    const uint32_t bg = (B - c0) < pl.bgroup ? (B - c0) : pl.bgroup;
-    const uint32_t bpad = (uint32_t)align_up(bg, 16);
+  uint32_t bg = 0;
+  for (uint32_t c0 = 0; c0 < B; c0 += bg) {
+    const uint32_t left = B - c0;
+    const bool wide = PACKED && pl.wide && left > kMfmaMaxCols;
+    const uint32_t cap = wide ? kWideCols : kMfmaMaxCols;
+    bg = left < cap ? left : cap;
+    const uint32_t bpad = wide ? kWideCols : (uint32_t)align_up(bg, 16);
     const uint64_t k16 = pl.kpad / 16;
-    hipLaunchKernelGGL(split_mfma_kernel, dim3(grid_for(k16 * bpad)), dim3(kThreads), 0, stream, query,
-                       dig, K, k16, bpad, bg, B, c0);
+    if (wide)
+      hipLaunchKernelGGL(split_wide_kernel, dim3(grid_for(k16 * bpad)), dim3(kThreads), 0, stream, query,
+                         reinterpret_cast<uint4*>(dig), K, k16, bpad, bg, B, c0);
+    else
+      hipLaunchKernelGGL(split_mfma_kernel, dim3(grid_for(k16 * bpad)), dim3(kThreads), 0, stream, query,
+                         dig, K, k16, bpad, bg, B, c0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint32_t* dst = pl.nkb > 1 ? part : out;
     timer_mark_start(stream);  // first pass only
-    switch (bpad) {
-      case 16: e = launch_mfma<4, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
-      case 32: e = launch_mfma<8, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
-      case 48: e = launch_mfma<12, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
-      default: e = launch_mfma<16, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+    if (wide) {
+      e = launch_mfma_wide(db, dig, dst, M, K, pl, bg, B, c0, stream);
+    } else {
+      switch (bpad) {
+        case 16: e = launch_mfma<4, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+        case 32: e = launch_mfma<8, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+        case 48: e = launch_mfma<12, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+        default: e = launch_mfma<16, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
+      }
     }
     if (e != hipSuccess) return e;
-    if (c0 + pl.bgroup >= B) timer_mark_stop(stream);  // last pass: before its reduction
+    if (c0 + bg >= B) timer_mark_stop(stream);  // last pass: before its reduction
     if (pl.nkb > 1) {
       hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(M * bg)), dim3(kThreads), 0, stream, part, out, M,
                          bg, pl.nkb, (uint64_t)B, c0);
@@ -694,12 +901,16 @@ hipError_t run_mfma_passes(const int8_t* db, const uint32_t* query, uint32_t* ou
   return hipSuccess;
 }
 
-// MFMA plan: up to kMfmaMaxCols columns per pass, K split only as far as the
-// tiles must be to fill the GPU.
-void mfma_plan(uint64_t M, uint64_t K, uint32_t B, ScalarPlan* p) {
+// MFMA plan: up to kMfmaMaxCols columns per pass (kWideCols with `wide`,
+// the tiled DB, when B > kMfmaMaxCols), K split only as far as the tiles
+// must be to fill the GPU.  The workspace holds the digit planes and partial
+// sums of the widest pass.
+void mfma_plan(uint64_t M, uint64_t K, uint32_t B, bool wide_ok, ScalarPlan* p) {
   p->mfma = true;
-  p->bgroup = B < kMfmaMaxCols ? B : kMfmaMaxCols;
-  p->bpad = (uint32_t)align_up(p->bgroup, 16);
+  p->wide = wide_ok && B > kMfmaMaxCols;
+  const uint32_t cap = p->wide ? kWideCols : kMfmaMaxCols;
+  p->bgroup = B < cap ? B : cap;
+  p->bpad = p->wide ? kWideCols : (uint32_t)align_up(p->bgroup, 16);
   const uint64_t row_blocks = ceil_div(M, (uint64_t)kMfmaWaves * 16 * kMfmaRowTiles2);
   uint64_t nkb = ceil_div(kMfmaTargetTiles, row_blocks);
   const uint64_t chunks = ceil_div(K, kMfmaChunkK);
@@ -764,7 +975,7 @@ bool scalar_plan(uint64_t M, uint64_t K, uint32_t B, uintptr_t db_addr, ScalarPl
     p->part_bytes = p->nkb > 1 ? p->nkb * M * 4 : 0;
     p->total_bytes = align_up(p->digit_bytes, 256) + p->part_bytes;
   } else {
-    mfma_plan(M, K, B, p);
+    mfma_plan(M, K, B, false, p);
   }
   return true;
 }
@@ -816,7 +1027,7 @@ bool scalar_tiled_plan(uint64_t M, uint64_t K, uint32_t B, ScalarPlan* p) {
     return false;
   p->fast = true;
   if (B > 1) {
-    mfma_plan(M, K, B, p);
+    mfma_plan(M, K, B, true, p);
     return true;
   }
   // B == 1: GEMV over wavefronts of kTiledGemvTiles row tiles, K split into

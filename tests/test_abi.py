@@ -167,6 +167,10 @@ def test_scalar_tiled_sizes_and_validation():
     assert pirscan.scalar_tiled_workspace_bytes(32768, 32768, 1) == (32768 + 64) * 4 + 4 * 32768 * 4
     assert pirscan.scalar_tiled_workspace_bytes(4096, 8192, 1) == (8192 + 64) * 4   # one k-block: no partials
     assert pirscan.scalar_tiled_workspace_bytes(0, 16, 1) == 0
+    # more than 64 columns: passes of 128 (512 digit columns); the hint shape
+    # runs unsplit, the second fold in 4 k-blocks with 128-column partials
+    assert pirscan.scalar_tiled_workspace_bytes(1 << 20, 1 << 16, 1280) == (1 << 16) * 512
+    assert pirscan.scalar_tiled_workspace_bytes(32768, 1 << 17, 1281) == (1 << 17) * 512 + 4 * 32768 * 128 * 4
     L = pirscan.lib()
     A = 1 << 40   # never dereferenced: every call below fails validation first
     vp = ctypes.c_void_p
