@@ -126,9 +126,9 @@ uint32_t rowsel_fold_period(uint32_t q);
 struct ScalarPlan {
   bool fast;          // aligned fast paths (K % 16 == 0, 16-byte aligned db)
   bool mfma;          // B > 1 on int8 MFMA
-  bool wide;          // passes of 128 columns while more than 64 remain (tiled DB)
-  uint32_t bgroup;    // columns per MFMA pass (<= 64)
-  uint32_t bpad;      // bgroup rounded up to 16
+  bool wide;          // wide passes (groups of 128 columns) while more than 64 remain (tiled DB)
+  uint32_t bgroup;    // columns of the widest pass
+  uint32_t bpad;      // its digit columns per plane: bgroup rounded up to 16, or whole 128-column groups
   uint64_t kblock;    // split-K block (k per partial sum)
   uint64_t nkb;       // number of k blocks
   uint64_t kpad;      // nkb * kblock

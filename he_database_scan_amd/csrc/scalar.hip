@@ -499,12 +499,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(const int8_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// S3, wide passes (more than 64 query columns, tiled DB): passes of 128 query
-// columns, so a batch of n columns streams the DB ceil(n / 128) times instead
-// of ceil(n / 64).  A tile = 128 rows (8 row tiles, half a tile group of the
-// tiled layout) x 512 digit columns (4 planes x 128 columns) of one k-block,
-// 8 wavefronts: wave w accumulates all 8 row tiles against planes 0..3 of
-// query columns 16w..16w+15 (one column tile per plane), 32 accumulator tiles.
+// S3, wide passes (more than 64 query columns, tiled DB): tiles of 128 query
+// columns, and one launch takes up to kWideGroups such column groups, so a
+// batch of n columns streams the DB from HBM about ceil(n / 512) times
+// instead of ceil(n / 64).  A tile = 128 rows (8 row tiles, half a tile group
+// of the tiled layout) x 512 digit columns (4 planes x 128 columns) of one
+// k-block, 8 wavefronts: wave w accumulates all 8 row tiles against planes
+// 0..3 of query columns 16w..16w+15 of its group (one column tile per plane),
+// 32 accumulator tiles.  The column groups of one row block are neighbouring
+// tiles, run side by side on one XCD: the first to read a DB fragment brings
+// it into that XCD's L2 for the others.  (Under sustained matrix load the
+// chip's clock is held by its power budget; the HBM reads saved this way
+// raise it.)
 //  * DB fragments (the A operand, used by all 8 waves) come into a six-step
 //    LDS ring once per workgroup with direct global-to-LDS loads, one 1 KiB
 //    fragment per wave per step, four steps ahead.
@@ -521,11 +527,15 @@ constexpr int kWidePlanes = 4;                 // column tiles per wave: one per
 constexpr uint64_t kWideRows = kWideRowTiles * 16;  // rows per tile: 128
 constexpr int kWideARing = 6;                  // A ring depth (LDS) in 64-k steps: loads 4 steps ahead
 constexpr int kWideBRing = 3;                  // B ring depth (registers): loads 2 steps ahead
+#ifndef PIRSCAN_WIDE_GROUPS
+#define PIRSCAN_WIDE_GROUPS 4
+#endif
+constexpr uint32_t kWideGroups = PIRSCAN_WIDE_GROUPS;  // 128-column groups per wide launch
 
 __device__ __forceinline__ void wide_tile(const v4i* __restrict__ dbp, const v4i* dig, uint32_t* __restrict__ dst,
                                           uint64_t M, uint64_t kblock, uint64_t nkb, uint32_t bgroup, uint64_t ldd,
-                                          uint32_t dcol0, uint64_t kb, uint64_t rb, uint64_t psteps,
-                                          v4i (*aring)[kWideWaves * 64]) {
+                                          uint32_t dcol0, uint64_t kb, uint64_t rb, uint32_t g, uint32_t ctiles,
+                                          uint64_t psteps, v4i (*aring)[kWideWaves * 64]) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane % 16, lg = lane / 16;
@@ -535,10 +545,10 @@ __device__ __forceinline__ void wide_tile(const v4i* __restrict__ dbp, const v4i
   const uint64_t t0 = rb * 8;
   const v4i* abase = dbp + ((t0 / kScalarGroupTiles) * psteps * kScalarGroupTiles + t0 % kScalarGroupTiles + wave) * 64 +
                      lane;
-  // digits in B-fragment order (split_wide_kernel): fragment (step, plane j,
-  // column tile w) is 1 KiB of contiguous lanes
-  constexpr uint32_t kCt = kWideCols / 16;
-  const v4i* bbase = dig + (uint64_t)wave * 64 + lane;
+  // digits in B-fragment order (split_wide_kernel, ctiles column tiles per
+  // plane): this wave's fragment (step, plane j) is column tile 8g + w, 1 KiB
+  // of contiguous lanes
+  const v4i* bbase = dig + (uint64_t)(kWideCols / 16 * g + wave) * 64 + lane;
 
   v4i acc[kWideRowTiles][kWidePlanes];
 #pragma unroll
@@ -557,9 +567,9 @@ __device__ __forceinline__ void wide_tile(const v4i* __restrict__ dbp, const v4i
   v4i bb[kWideBRing][kWidePlanes];
   auto load_b = [&](int slot, uint32_t s) {
     const uint32_t ss = s < nsteps ? s : nsteps - 1;  // past the end: a harmless reload
-    const v4i* bs = bbase + (s_first + ss) * (4ull * kCt * 64);
+    const v4i* bs = bbase + (s_first + ss) * (4ull * ctiles * 64);
 #pragma unroll
-    for (int j = 0; j < kWidePlanes; ++j) bb[slot][j] = bs[j * kCt * 64];
+    for (int j = 0; j < kWidePlanes; ++j) bb[slot][j] = bs[(uint64_t)j * ctiles * 64];
   };
   // One step.  Per step B(s+2) (4 loads), then A(s+4) (1) are issued.  At
   // the wait of step s the loads issued after B(s) are A(s+2), B(s+1) and
@@ -607,8 +617,8 @@ __device__ __forceinline__ void wide_tile(const v4i* __restrict__ dbp, const v4i
   __syncthreads();                // the next tile's prologue overwrites the ring
 
   // D element i of lane l is (row 4*(l/16) + i, column l%16) of a tile;
-  // this wave's column tile j is plane j of query columns 16w + 0..15
-  const uint32_t b = 16 * wave + li;
+  // this wave's column tile j is plane j of query columns 128g + 16w + 0..15
+  const uint32_t b = kWideCols * g + 16 * wave + li;
   if (b >= bgroup) return;
 #pragma unroll
   for (int rt = 0; rt < kWideRowTiles; ++rt) {
@@ -629,16 +639,23 @@ __global__ __launch_bounds__(64 * kWideWaves) void mfma_wide_kernel(const v4i* _
                                                                      uint32_t* __restrict__ dst, uint64_t M,
                                                                      uint64_t kblock, uint64_t nkb,
                                                                      uint64_t row_blocks, uint32_t bgroup,
-                                                                     uint64_t ldd, uint32_t dcol0, uint64_t psteps) {
+                                                                     uint64_t ldd, uint32_t dcol0, uint64_t psteps,
+                                                                     uint32_t groups) {
   __shared__ v4i aring[kWideARing][kWideWaves * 64];
   constexpr uint32_t kXcds = 8;
   const uint32_t hw = blockIdx.x, G = gridDim.x;  // G >= kXcds (host guarantees)
   const uint32_t xcd = hw % kXcds, j = hw / kXcds;
   const uint32_t per_xcd = (G - xcd + kXcds - 1) / kXcds;
-  const uint64_t tiles = nkb * row_blocks;
+  // tile t: column group t % groups (fastest, so that the workgroups of one
+  // row block's groups run side by side on one XCD and read its DB
+  // fragments from HBM once), then row block, then k-block
+  const uint64_t tiles = nkb * row_blocks * groups;
   const uint64_t lo = tiles * xcd / kXcds, hi = tiles * (xcd + 1) / kXcds;
-  for (uint64_t t = lo + j; t < hi; t += per_xcd)
-    wide_tile(dbp, dig, dst, M, kblock, nkb, bgroup, ldd, dcol0, t / row_blocks, t % row_blocks, psteps, aring);
+  for (uint64_t t = lo + j; t < hi; t += per_xcd) {
+    const uint64_t r = t / groups;
+    wide_tile(dbp, dig, dst, M, kblock, nkb, bgroup, ldd, dcol0, r / row_blocks, r % row_blocks,
+              (uint32_t)(t % groups), 8 * groups, psteps, aring);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -731,18 +748,18 @@ hipError_t launch_mfma(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint
 }
 
 hipError_t launch_mfma_wide(const int8_t* db, const uint8_t* dig, uint32_t* dst, uint64_t M, uint64_t K,
-                            const ScalarPlan& pl, uint32_t bgroup, uint64_t ldd, uint32_t dcol0,
+                            const ScalarPlan& pl, uint32_t bgroup, uint32_t groups, uint64_t ldd, uint32_t dcol0,
                             hipStream_t stream) {
   const uint64_t row_blocks = ceil_div(M, kWideRows);
   if (pl.kblock % 64 != 0) return hipErrorInvalidValue;
   uint64_t grid = 0;
   const hipError_t e = resident_workgroups<mfma_wide_kernel, 64 * kWideWaves>(&grid);
   if (e != hipSuccess) return e;
-  if (grid > row_blocks * pl.nkb) grid = row_blocks * pl.nkb;
+  if (grid > row_blocks * pl.nkb * groups) grid = row_blocks * pl.nkb * groups;
   if (grid < 8) grid = 8;
   hipLaunchKernelGGL(mfma_wide_kernel, dim3((uint32_t)grid), dim3(64 * kWideWaves), 0, stream,
                      reinterpret_cast<const v4i*>(db), reinterpret_cast<const v4i*>(dig), dst, M, pl.kblock, pl.nkb,
-                     row_blocks, bgroup, ldd, dcol0, ceil_div(K, 64));
+                     row_blocks, bgroup, ldd, dcol0, ceil_div(K, 64), groups);
   return hipGetLastError();
 }
 
@@ -856,9 +873,24 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(const u32x4* __res
   }
 }
 
+// Columns of the next wide launch with `left` (> kMfmaMaxCols) columns to
+// go, and its 128-column groups: whole groups up to kWideGroups, plus a
+// partial group when more than kMfmaMaxCols of it remain (a smaller
+// remainder takes a narrow pass).
+uint32_t wide_launch(uint32_t left, uint32_t* groups) {
+  const uint32_t full = left / kWideCols, rem = left % kWideCols;
+  if (full >= kWideGroups) {
+    *groups = kWideGroups;
+    return kWideGroups * kWideCols;
+  }
+  *groups = full + (rem > kMfmaMaxCols ? 1u : 0u);
+  return rem > kMfmaMaxCols ? left : full * kWideCols;
+}
+
 // The MFMA passes: digit split, scan, split-K reduction.  Passes take up to
-// kMfmaMaxCols query columns, or kWideCols on the tiled DB while more than
-// kMfmaMaxCols columns remain (the plan's `wide`).
+// kMfmaMaxCols query columns, or on the tiled DB, while more than
+// kMfmaMaxCols columns remain (the plan's `wide`), up to kWideGroups groups
+// of kWideCols (wide_launch).
 template <bool PACKED>
 hipError_t run_mfma_passes(const int8_t* db, const uint32_t* query, uint32_t* out, uint64_t M, uint64_t K,
                            uint32_t B, const ScalarPlan& pl, uint8_t* dig, uint32_t* part, hipStream_t stream) {
@@ -867,9 +899,9 @@ hipError_t run_mfma_passes(const int8_t* db, const uint32_t* query, uint32_t* ou
   for (uint32_t c0 = 0; c0 < B; c0 += bg) {
     const uint32_t left = B - c0;
     const bool wide = PACKED && pl.wide && left > kMfmaMaxCols;
-    const uint32_t cap = wide ? kWideCols : kMfmaMaxCols;
-    bg = left < cap ? left : cap;
-    const uint32_t bpad = wide ? kWideCols : (uint32_t)align_up(bg, 16);
+    uint32_t groups = 1;
+    bg = wide ? wide_launch(left, &groups) : (left < kMfmaMaxCols ? left : kMfmaMaxCols);
+    const uint32_t bpad = wide ? groups * kWideCols : (uint32_t)align_up(bg, 16);
     const uint64_t k16 = pl.kpad / 16;
     if (wide)
       hipLaunchKernelGGL(split_wide_kernel, dim3(grid_for(k16 * bpad)), dim3(kThreads), 0, stream, query,
@@ -881,7 +913,7 @@ hipError_t run_mfma_passes(const int8_t* db, const uint32_t* query, uint32_t* ou
     uint32_t* dst = pl.nkb > 1 ? part : out;
     timer_mark_start(stream);  // first pass only
     if (wide) {
-      e = launch_mfma_wide(db, dig, dst, M, K, pl, bg, B, c0, stream);
+      e = launch_mfma_wide(db, dig, dst, M, K, pl, bg, groups, B, c0, stream);
     } else {
       switch (bpad) {
         case 16: e = launch_mfma<4, PACKED>(db, dig, dst, M, K, pl, bg, B, c0, stream); break;
@@ -908,9 +940,14 @@ hipError_t run_mfma_passes(const int8_t* db, const uint32_t* query, uint32_t* ou
 void mfma_plan(uint64_t M, uint64_t K, uint32_t B, bool wide_ok, ScalarPlan* p) {
   p->mfma = true;
   p->wide = wide_ok && B > kMfmaMaxCols;
-  const uint32_t cap = p->wide ? kWideCols : kMfmaMaxCols;
-  p->bgroup = B < cap ? B : cap;
-  p->bpad = p->wide ? kWideCols : (uint32_t)align_up(p->bgroup, 16);
+  if (p->wide) {  // the first launch is the widest
+    uint32_t groups = 1;
+    p->bgroup = wide_launch(B, &groups);
+    p->bpad = groups * kWideCols;
+  } else {
+    p->bgroup = B < kMfmaMaxCols ? B : kMfmaMaxCols;
+    p->bpad = (uint32_t)align_up(p->bgroup, 16);
+  }
   const uint64_t row_blocks = ceil_div(M, (uint64_t)kMfmaWaves * 16 * kMfmaRowTiles2);
   uint64_t nkb = ceil_div(kMfmaTargetTiles, row_blocks);
   const uint64_t chunks = ceil_div(K, kMfmaChunkK);

@@ -284,8 +284,8 @@ int pirscan_scalar_gemm_u32_noalloc(const int8_t* db, const uint32_t* query, uin
 size_t pirscan_scalar_layout_db_bytes(uint64_t M, uint64_t K);
 int pirscan_scalar_layout_db(const int8_t* db, void* db_tiled, uint64_t M, uint64_t K, void* stream);
 /* Workspace bytes pirscan_scalar_gemm_u32_tiled needs for (M, K, B): the
- * signed digit planes of one pass (up to 64 query columns, or 128 when B > 64)
- * plus split-K partial sums.  0 on invalid sizes. */
+ * signed digit planes of the widest pass (up to 64 query columns; when B > 64,
+ * up to four groups of 128) plus split-K partial sums.  0 on invalid sizes. */
 size_t pirscan_scalar_tiled_workspace_bytes(uint64_t M, uint64_t K, uint32_t B);
 /*
  * The scalar-HE product on the tiled DB: the same result as

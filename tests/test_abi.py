@@ -167,10 +167,16 @@ def test_scalar_tiled_sizes_and_validation():
     assert pirscan.scalar_tiled_workspace_bytes(32768, 32768, 1) == (32768 + 64) * 4 + 4 * 32768 * 4
     assert pirscan.scalar_tiled_workspace_bytes(4096, 8192, 1) == (8192 + 64) * 4   # one k-block: no partials
     assert pirscan.scalar_tiled_workspace_bytes(0, 16, 1) == 0
-    # more than 64 columns: passes of 128 (512 digit columns); the hint shape
-    # runs unsplit, the second fold in 4 k-blocks with 128-column partials
-    assert pirscan.scalar_tiled_workspace_bytes(1 << 20, 1 << 16, 1280) == (1 << 16) * 512
-    assert pirscan.scalar_tiled_workspace_bytes(32768, 1 << 17, 1281) == (1 << 17) * 512 + 4 * 32768 * 128 * 4
+    # more than 64 columns: passes of up to four 128-column groups (2048 digit
+    # columns); the hint shape runs unsplit, the second fold in 4 k-blocks with
+    # 512-column partials
+    assert pirscan.scalar_tiled_workspace_bytes(1 << 20, 1 << 16, 1280) == (1 << 16) * 2048
+    assert pirscan.scalar_tiled_workspace_bytes(32768, 1 << 17, 1281) == (1 << 17) * 2048 + 4 * 32768 * 512 * 4
+    # one group and a partial one (more than 64 columns left: 256 digit
+    # columns, 200-column partials), or one group and a narrow remainder (64 or
+    # fewer); 4096 rows split K into 16 k-blocks of 256
+    assert pirscan.scalar_tiled_workspace_bytes(4096, 4096, 200) == 4096 * 4 * 256 + 16 * 4096 * 200 * 4
+    assert pirscan.scalar_tiled_workspace_bytes(4096, 4096, 150) == 4096 * 4 * 128 + 16 * 4096 * 128 * 4
     L = pirscan.lib()
     A = 1 << 40   # never dereferenced: every call below fails validation first
     vp = ctypes.c_void_p

@@ -54,14 +54,17 @@ def rand_case(seed, M, K, B):
 
 # (M, K, B): one row, ragged rows and k (K % 16 != 0 takes the byte-wise
 # packing), one to several 16-column tiles, a 64-column pass plus a ragged one,
-# and the 128-column passes of wide batches.
+# and the wide passes (up to four 128-column groups per launch) of wide batches.
 SHAPES = [(1, 1, 1), (1, 16, 1), (17, 65, 1), (63, 4096, 1), (300, 4096 * 3 + 48, 1), (257, 160, 1),
           (50, 1001, 1), (100, 64, 2), (130, 1040, 3), (64, 4096, 8), (333, 20000, 8), (65, 16400, 16),
           (200, 2048, 17), (129, 33024, 32), (70, 512, 33), (40, 800, 40), (17, 33, 5), (77, 4160, 64),
           (100, 2048, 65), (31, 300, 130),
-          # passes of 128 columns while more than 64 remain: one wide pass (65..128), wide passes plus a
-          # narrow remainder (130, 200, 1281), ragged rows past a 128-row tile, K not a multiple of 64
-          (129, 4160, 128), (257, 20480, 200), (100, 4096, 1280), (37, 1040, 1281), (300, 16400, 96)]
+          # wide launches while more than 64 columns remain: one group (65..128), a group plus a partial
+          # group of more than 64 (200), whole groups plus a narrow remainder (130, 300, 530, 1281), three
+          # groups (384), four groups and a partial launch (600), ragged rows past a 128-row tile, K not a
+          # multiple of 64
+          (129, 4160, 128), (257, 20480, 200), (100, 4096, 1280), (37, 1040, 1281), (300, 16400, 96),
+          (70, 1100, 300), (64, 4096, 384), (90, 2048, 530), (150, 4160, 600)]
 
 
 @pytest.mark.parametrize("M,K,B", SHAPES)
