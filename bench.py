@@ -511,7 +511,8 @@ SCAN_KERNELS = {
     **{name: CONFIG_SCANS[name] for name in ("scalar_64GiB_B1_rowmajor", "scalar_64GiB_B32_rowmajor",
                                              "scalar_1GiB_B1", "scalar_1GiB_B1_rowmajor", "scalar_1GiB_B8",
                                              "scalar_1GiB_B8_rowmajor", "rowsel_3GiB_B1", "rowsel_3GiB_B1_valu")},
-    **{name: ("gemv_tiled_kernel" if B == 1 else "mfma_kernel<8, true>" if B <= 32 else "mfma_kernel<16, true>")
+    **{name: ("gemv_tiled_kernel" if B == 1 else "mfma_kernel<8, true>" if B <= 32 else
+              "mfma_kernel<16, true>" if B <= 64 else "mfma_wide_kernel")
        for name, (M, K, B) in SHAPE_SCANS.items()},
     "rowsel_48GiB_B1_valu": CONFIG_SCANS["rowsel_48GiB_B1_valu"],
     "rowsel_48GiB_B16_valu": CONFIG_SCANS["rowsel_48GiB_B16_valu"],
