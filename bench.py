@@ -567,7 +567,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_gib: float) -> d
         return vals, first
 
     out = {"calibration": {}}
-    per = {}
+    per, every = {}, {}
     for kind, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         vals, first = load(path, counter)
         copies = [v for g, vs in vals.items() if "copy" in g[0].lower() for v in vs]
@@ -576,6 +576,11 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_gib: float) -> d
         scale = calib_gib * 2**30 / (max(copies) * 1024.0)  # true bytes per counted byte
         out["calibration"][counter] = {"copy_bytes": calib_gib * 2**30, "counter_KiB": max(copies),
                                        "scale": scale}
+        # every (kernel, grid) group of the run, the per-query passes around the
+        # main kernels included
+        for g, vs in vals.items():
+            e = every.setdefault(g, {"kernel": g[0], "grid_size": g[1], "launches": len(vs), "first": first[g]})
+            e[kind + "_bytes"] = statistics.median(vs) * 1024.0 * scale
         for scan, g in assign_scan_groups(first).items():
             per.setdefault(scan, {})[kind + "_bytes"] = statistics.median(vals[g]) * 1024.0 * scale
             per[scan]["kernel"] = g[0]
@@ -585,6 +590,9 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_gib: float) -> d
             ent["bytes_per_launch"] = ent["fetch_bytes"] + ent["write_bytes"]
             ent["source_sha256_16"] = source_hash(KERNEL_SOURCES[scan])
             out[scan] = ent
+    out["all_kernels"] = [{k: v for k, v in e.items() if k != "first"}
+                          for e in sorted(every.values(), key=lambda e: e["first"])
+                          if "fetch_bytes" in e and "write_bytes" in e]
     return out
 
 
