@@ -556,8 +556,10 @@ __device__ __forceinline__ void wide_tile(const v4i* __restrict__ dbp, const v4i
 #pragma unroll
     for (int j = 0; j < kWidePlanes; ++j) acc[rt][j] = v4i{0, 0, 0, 0};
 
-  // step s's DB fragments -> LDS ring slot s % 3; wave w moves fragment w.
-  // Past the DB's last step the last one is read again: it meets zero digits.
+  // step s's DB fragments -> LDS ring slot s % kWideARing; wave w moves
+  // fragment w.  The ring runs four steps ahead, so the last steps load
+  // fragments past this k-block that no MFMA reads; past the DB's last step
+  // the address is clamped to stay inside the buffer.
   auto issue_a = [&](uint32_t s) {
     uint64_t sg = s_first + s;
     sg = sg < psteps ? sg : psteps - 1;
