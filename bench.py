@@ -516,9 +516,9 @@ SCAN_KERNELS = {
        for name, (M, K, B) in SHAPE_SCANS.items()},
     "rowsel_48GiB_B1_valu": CONFIG_SCANS["rowsel_48GiB_B1_valu"],
     "rowsel_48GiB_B16_valu": CONFIG_SCANS["rowsel_48GiB_B16_valu"],
-    "ntt_rns_fwd_hint": "ntt_rns_kernel<12>",
-    "ntt_inv_hint": "ntt_kernel<12, true>",
-    "ntt_fwd_hint": "ntt_kernel<12, false>",
+    "ntt_rns_fwd_hint": "ntt_rns_kernel<12",
+    "ntt_inv_hint": "ntt_kernel<12, true",
+    "ntt_fwd_hint": "ntt_kernel<12, false",
 }
 
 

@@ -30,6 +30,18 @@
 // w' = floor(w 2^32 / q): y w mod q = y w - mulhi(y, w') q in [0, 2q) for any
 // 32-bit y.  Butterflies keep residues lazily in [0, 4q) (forward) or
 // [0, 2q) (inverse) and the output is made canonical, [0, q), once at the end.
+// With every q <= 2^29 (8q fits in 32 bits) the bounds are looser, which
+// saves conditional subtractions:
+//  * forward: a butterfly on inputs below b gives outputs below b + 2q (the
+//    Shoup product is below 2q), so from inputs below 2q three stages run
+//    with no reduction (to 8q); after that every other stage first brings X
+//    below 4q (outputs below 6q) and the stage between lets it grow to 8q;
+//  * inverse: the sum path doubles per stage, so the first two stages (from
+//    canonical inputs: below 2q, then 4q) skip its reduction and later ones
+//    reduce it below 4q; the difference path is offset by the bound of Y
+//    before its Shoup product.
+// The inverse's last stage (a single twiddle) multiplies both outputs by
+// N^-1 (its twiddle premultiplied), so no separate scaling pass follows.
 // VIPIR uses Montgomery multiplication inside its NTT; with twiddles that are
 // known ahead of time, Shoup's precomputed quotient needs the same three
 // 32-bit multiplies and no domain conversion.
@@ -74,13 +86,18 @@ __device__ __forceinline__ uint32_t bit_reverse(uint32_t x, int n) { return n ? 
 // One round of forward (CT) stages on index bits BHI down to BLO, with the
 // thread's elements varying in bits [LO, LO+4).  When the thread's index bits
 // all lie below LO (the first round), the twiddle index is wave-uniform.
-template <int LOGN, int LO, int BHI, int BLO>
+// Forward stage number s (0 first) reduces X before its butterfly: always
+// with q < 2^30 (below 2q), with q <= 2^29 (LAZY) at s = 3, 5, 7, ... (below 4q).
+__host__ __device__ constexpr bool fwd_reduces(int s, bool lazy) { return !lazy || (s >= 3 && (s - 3) % 2 == 0); }
+
+template <int LOGN, int LO, int BHI, int BLO, bool LAZY>
 __device__ __forceinline__ void fwd_round(uint32_t (&x)[kElems], uint32_t tid, const uint2* __restrict__ tw,
                                           uint32_t q) {
-  const uint32_t q2 = 2 * q;
+  const uint32_t q2 = 2 * q, red = LAZY ? 4 * q : 2 * q;
 #pragma unroll
   for (int b = BHI; b >= BLO; --b) {
     const uint32_t m = 1u << (LOGN - 1 - b);
+    const bool reduce = fwd_reduces(LOGN - 1 - b, LAZY);
 #pragma unroll
     for (int e = 0; e < kElems; ++e) {
       if ((e >> (b - LO)) & 1) continue;
@@ -89,7 +106,7 @@ __device__ __forceinline__ void fwd_round(uint32_t (&x)[kElems], uint32_t tid, c
       if constexpr (LO == LOGN - 4) t = m + (uint32_t)(e >> (b - LO + 1));
       else t = m + ((tid >> LO) << (LO + 3 - b)) + (uint32_t)(e >> (b - LO + 1));
       const uint2 w = tw[t];
-      const uint32_t X = sub_if_ge(x[e], q2);
+      const uint32_t X = reduce ? sub_if_ge(x[e], red) : x[e];
       const uint32_t nV = mul_shoup_neg(x[e2], w.x, w.y, q);
       x[e] = X - nV;
       x[e2] = X + nV + q2;
@@ -97,14 +114,27 @@ __device__ __forceinline__ void fwd_round(uint32_t (&x)[kElems], uint32_t tid, c
   }
 }
 
-// One round of inverse (GS) stages on index bits BLO up to BHI.
-template <int LOGN, int LO, int BLO, int BHI>
+// The inverse's last stage (index bit LOGN-1, the single twiddle w1 =
+// psi^-(N/2)): both outputs times N^-1, the twiddle premultiplied.
+struct InvLast {
+  uint32_t ninv, ninv_q;  // N^-1 mod q and its Shoup quotient
+  uint32_t w, w_q;        // w1 N^-1 mod q and its Shoup quotient
+};
+
+// One round of inverse (GS) stages on index bits BLO up to BHI (stage number
+// = bit).  With q < 2^30 inputs are below 2q and every stage reduces the sum
+// below 2q; with q <= 2^29 (LAZY) stages 0 and 1 let the sum grow (below 2q,
+// then 4q) and later ones reduce it below 4q, the difference offset by Y's
+// bound (2q, then 4q).
+template <int LOGN, int LO, int BLO, int BHI, bool LAZY>
 __device__ __forceinline__ void inv_round(uint32_t (&x)[kElems], uint32_t tid, const uint2* __restrict__ tw,
-                                          uint32_t q) {
-  const uint32_t q2 = 2 * q;
+                                          uint32_t q, const InvLast& last) {
 #pragma unroll
   for (int b = BLO; b <= BHI; ++b) {
     const uint32_t h = 1u << (LOGN - 1 - b);
+    const bool reduce = !LAZY || b >= 2;
+    const uint32_t red = LAZY ? 4 * q : 2 * q;
+    const uint32_t off = (LAZY && b >= 2) ? 4 * q : 2 * q;
 #pragma unroll
     for (int e = 0; e < kElems; ++e) {
       if ((e >> (b - LO)) & 1) continue;
@@ -112,10 +142,15 @@ __device__ __forceinline__ void inv_round(uint32_t (&x)[kElems], uint32_t tid, c
       uint32_t t;
       if constexpr (LO == LOGN - 4) t = h + (uint32_t)(e >> (b - LO + 1));
       else t = h + ((tid >> LO) << (LO + 3 - b)) + (uint32_t)(e >> (b - LO + 1));
-      const uint2 w = tw[t];
       const uint32_t X = x[e], Y = x[e2];
-      x[e] = sub_if_ge(X + Y, q2);
-      x[e2] = mul_shoup(X - Y + q2, w.x, w.y, q);
+      if (b == LOGN - 1) {  // outputs below 2q
+        x[e] = mul_shoup(X + Y, last.ninv, last.ninv_q, q);
+        x[e2] = mul_shoup(X - Y + off, last.w, last.w_q, q);
+      } else {
+        const uint2 w = tw[t];
+        x[e] = reduce ? sub_if_ge(X + Y, red) : X + Y;
+        x[e2] = mul_shoup(X - Y + off, w.x, w.y, q);
+      }
     }
   }
 }
@@ -169,25 +204,25 @@ struct InvRound {
   static constexpr int lo = (bhi + 1 - blo == 4) ? blo : LOGN - 4;
 };
 
-template <int LOGN, int R>
+template <int LOGN, int R, bool LAZY>
 __device__ __forceinline__ void fwd_rounds_from(uint32_t (&x)[kElems], uint32_t tid, const uint2* tw, uint32_t q,
                                                 uint32_t* lds) {
   if constexpr (FwdRound<LOGN, R>::hi > 0) {
     using C = FwdRound<LOGN, R>;
     if constexpr (R > 0) exchange<FwdRound<LOGN, R - 1>::lo, C::lo>(x, tid, lds);
-    fwd_round<LOGN, C::lo, C::hi - 1, C::blo>(x, tid, tw, q);
-    fwd_rounds_from<LOGN, R + 1>(x, tid, tw, q, lds);
+    fwd_round<LOGN, C::lo, C::hi - 1, C::blo, LAZY>(x, tid, tw, q);
+    fwd_rounds_from<LOGN, R + 1, LAZY>(x, tid, tw, q, lds);
   }
 }
 
-template <int LOGN, int R>
+template <int LOGN, int R, bool LAZY>
 __device__ __forceinline__ void inv_rounds_from(uint32_t (&x)[kElems], uint32_t tid, const uint2* tw, uint32_t q,
-                                                uint32_t* lds) {
+                                                const InvLast& last, uint32_t* lds) {
   if constexpr (4 * R < LOGN) {
     using C = InvRound<LOGN, R>;
     if constexpr (R > 0) exchange<InvRound<LOGN, R - 1>::lo, C::lo>(x, tid, lds);
-    inv_round<LOGN, C::lo, C::blo, C::bhi>(x, tid, tw, q);
-    inv_rounds_from<LOGN, R + 1>(x, tid, tw, q, lds);
+    inv_round<LOGN, C::lo, C::blo, C::bhi, LAZY>(x, tid, tw, q, last);
+    inv_rounds_from<LOGN, R + 1, LAZY>(x, tid, tw, q, last, lds);
   }
 }
 
@@ -196,13 +231,19 @@ constexpr int last_fwd_lo() {
   return FwdRound<LOGN, (LOGN + 3) / 4 - 1>::lo;
 }
 
-// Forward transform of x (the coalesced mapping on entry, residues < 4q) and
+// Forward transform of x (the coalesced mapping on entry, residues < 2q) and
 // store: out[j] = A[j] in natural order, canonical.
-template <int LOGN>
+template <int LOGN, bool LAZY>
+__device__ __forceinline__ uint32_t fwd_canonical(uint32_t v, uint32_t q) {
+  if constexpr (LAZY) v = sub_if_ge(v, 4 * q);  // below 8q
+  return sub_if_ge(sub_if_ge(v, 2 * q), q);      // below 4q
+}
+
+template <int LOGN, bool LAZY>
 __device__ __forceinline__ void forward_and_store(uint32_t (&x)[kElems], uint32_t tid, const uint2* tw,
                                                   uint32_t q, uint32_t* lds, uint32_t* __restrict__ dst) {
   constexpr uint32_t T = 1u << (LOGN - 4);
-  fwd_rounds_from<LOGN, 0>(x, tid, tw, q, lds);
+  fwd_rounds_from<LOGN, 0, LAZY>(x, tid, tw, q, lds);
   // canonical, then to natural order: element j holds A[bitrev(j)]
   constexpr int LL = last_fwd_lo<LOGN>();
   __syncthreads();
@@ -211,11 +252,11 @@ __device__ __forceinline__ void forward_and_store(uint32_t (&x)[kElems], uint32_
     const uint32_t wb = (uint32_t)pad_index((int)bit_reverse(tid, LOGN - 4));
 #pragma unroll
     for (int e = 0; e < kElems; ++e)
-      lds[wb + bit_reverse4(e) * ((1 << (LOGN - 4)) + (1 << (LOGN - 8)))] = sub_if_ge(sub_if_ge(x[e], 2 * q), q);
+      lds[wb + bit_reverse4(e) * ((1 << (LOGN - 4)) + (1 << (LOGN - 8)))] = fwd_canonical<LOGN, LAZY>(x[e], q);
   } else {
 #pragma unroll
     for (int e = 0; e < kElems; ++e) {
-      const uint32_t v = sub_if_ge(sub_if_ge(x[e], 2 * q), q);
+      const uint32_t v = fwd_canonical<LOGN, LAZY>(x[e], q);
       lds[pad_index((int)bit_reverse(elem_index<LL>(tid, e), LOGN))] = v;
     }
   }
@@ -237,11 +278,13 @@ struct NttArgs {
   uint32_t R;
   uint32_t q[kMaxLimbs];
   uint32_t ninv[kMaxLimbs], ninv_q[kMaxLimbs];  // N^-1 mod q and its Shoup quotient
+  uint32_t w1n[kMaxLimbs], w1n_q[kMaxLimbs];    // psi^-(N/2) N^-1 mod q and its Shoup quotient
   uint32_t one_q[kMaxLimbs];                    // floor(2^32 / q): x mod q in [0, 2q) for x < 2^32
 };
 
-// Residue transforms: one workgroup per (polynomial, limb) row.
-template <int LOGN, bool INVERSE>
+// Residue transforms: one workgroup per (polynomial, limb) row.  LAZY: every
+// q <= 2^29.
+template <int LOGN, bool INVERSE, bool LAZY>
 __global__ __launch_bounds__(1 << (LOGN - 4)) void ntt_kernel(NttArgs a) {
   constexpr uint32_t N = 1u << LOGN, T = N >> 4;
   __shared__ uint32_t lds[pad_index((int)N)];
@@ -256,7 +299,7 @@ __global__ __launch_bounds__(1 << (LOGN - 4)) void ntt_kernel(NttArgs a) {
     const uint2* tw = a.plan + (uint64_t)(2 * r) * N;
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = __builtin_nontemporal_load(src + tid + T * (uint32_t)e);
-    forward_and_store<LOGN>(x, tid, tw, q, lds, dst);
+    forward_and_store<LOGN, LAZY>(x, tid, tw, q, lds, dst);
   } else {
     const uint2* tw = a.plan + (uint64_t)(2 * r + 1) * N;
     // scatter the natural-order input to bit-reversed positions
@@ -271,18 +314,18 @@ __global__ __launch_bounds__(1 << (LOGN - 4)) void ntt_kernel(NttArgs a) {
     const uint32_t rb = lds_base<L0>(tid);
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = *lds_slot<L0>(lds, rb, tid, e);
-    inv_rounds_from<LOGN, 0>(x, tid, tw, q, lds);
+    const InvLast last{a.ninv[r], a.ninv_q[r], a.w1n[r], a.w1n_q[r]};
+    inv_rounds_from<LOGN, 0, LAZY>(x, tid, tw, q, last, lds);
     // the last round's mapping is lo = LOGN - 4: element e sits at tid + T e
     static_assert(InvRound<LOGN, (LOGN + 3) / 4 - 1>::lo == LOGN - 4, "inverse ends coalesced");
-    const uint32_t ni = a.ninv[r], niq = a.ninv_q[r];
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) dst[tid + T * (uint32_t)e] = sub_if_ge(mul_shoup(x[e], ni, niq, q), q);
+    for (int e = 0; e < kElems; ++e) dst[tid + T * (uint32_t)e] = sub_if_ge(x[e], q);  // scaled: below 2q
   }
 }
 
 // RNS decomposition fused with the forward transform: one workgroup per
 // polynomial reads its N integer coefficients once and writes all R limbs.
-template <int LOGN>
+template <int LOGN, bool LAZY>
 __global__ __launch_bounds__(1 << (LOGN - 4)) void ntt_rns_kernel(NttArgs a) {
   constexpr uint32_t N = 1u << LOGN, T = N >> 4;
   __shared__ uint32_t lds[pad_index((int)N)];
@@ -297,13 +340,13 @@ __global__ __launch_bounds__(1 << (LOGN - 4)) void ntt_rns_kernel(NttArgs a) {
     uint32_t x[kElems];
 #pragma unroll
     for (int e = 0; e < kElems; ++e) x[e] = coef[e] - __umulhi(coef[e], oq) * q;  // [0, 2q)
-    forward_and_store<LOGN>(x, tid, a.plan + (uint64_t)(2 * r) * N, q, lds, a.out + (c * a.R + r) * N);
+    forward_and_store<LOGN, LAZY>(x, tid, a.plan + (uint64_t)(2 * r) * N, q, lds, a.out + (c * a.R + r) * N);
   }
 }
 
 // Plan: for limb r and k < N, (w, floor(w 2^32 / q)) with w = psi^bitrev(k)
 // (forward) and psi^-bitrev(k) (inverse), psi^-1 = psi^(2N-1).
-__device__ uint32_t pow_mod(uint32_t b, uint32_t e, uint32_t q) {
+__host__ __device__ uint32_t pow_mod(uint32_t b, uint32_t e, uint32_t q) {
   uint64_t r = 1 % q, x = b % q;
   while (e) {
     if (e & 1) r = (r * x) % q;
@@ -329,7 +372,7 @@ __global__ void ntt_plan_kernel(uint2* __restrict__ plan, uint32_t logn, uint32_
   }
 }
 
-template <int LOGN>
+template <int LOGN, bool LAZY>
 hipError_t launch_for(const NttArgs& a, NttMode mode, hipStream_t stream) {
   constexpr uint32_t T = 1u << (LOGN - 4);
   const uint64_t blocks = mode == NttMode::kRnsForward ? a.count : a.count * a.R;
@@ -337,16 +380,21 @@ hipError_t launch_for(const NttArgs& a, NttMode mode, hipStream_t stream) {
   if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
   switch (mode) {
     case NttMode::kForward:
-      hipLaunchKernelGGL((ntt_kernel<LOGN, false>), dim3((uint32_t)blocks), dim3(T), 0, stream, a);
+      hipLaunchKernelGGL((ntt_kernel<LOGN, false, LAZY>), dim3((uint32_t)blocks), dim3(T), 0, stream, a);
       break;
     case NttMode::kInverse:
-      hipLaunchKernelGGL((ntt_kernel<LOGN, true>), dim3((uint32_t)blocks), dim3(T), 0, stream, a);
+      hipLaunchKernelGGL((ntt_kernel<LOGN, true, LAZY>), dim3((uint32_t)blocks), dim3(T), 0, stream, a);
       break;
     case NttMode::kRnsForward:
-      hipLaunchKernelGGL((ntt_rns_kernel<LOGN>), dim3((uint32_t)blocks), dim3(T), 0, stream, a);
+      hipLaunchKernelGGL((ntt_rns_kernel<LOGN, LAZY>), dim3((uint32_t)blocks), dim3(T), 0, stream, a);
       break;
   }
   return hipGetLastError();
+}
+
+template <int LOGN>
+hipError_t launch_for(const NttArgs& a, bool lazy, NttMode mode, hipStream_t stream) {
+  return lazy ? launch_for<LOGN, true>(a, mode, stream) : launch_for<LOGN, false>(a, mode, stream);
 }
 
 }  // namespace
@@ -372,25 +420,33 @@ hipError_t launch_ntt(const NttDesc& d, NttMode mode, const void* plan, const ui
   a.plan = static_cast<const uint2*>(plan);
   a.count = count;
   a.R = d.R;
+  bool lazy = true;  // every q <= 2^29: 8q fits in 32 bits
   for (uint32_t r = 0; r < d.R; ++r) {
-    a.q[r] = d.q[r];
+    const uint32_t q = d.q[r];
+    a.q[r] = q;
     a.ninv[r] = d.ninv[r];
-    a.ninv_q[r] = (uint32_t)(((uint64_t)d.ninv[r] << 32) / d.q[r]);
-    a.one_q[r] = (uint32_t)((1ull << 32) / d.q[r]);
+    a.ninv_q[r] = (uint32_t)(((uint64_t)d.ninv[r] << 32) / q);
+    a.one_q[r] = (uint32_t)((1ull << 32) / q);
+    // the inverse's last twiddle, psi^-bitrev(1) = (psi^-1)^(N/2) as the plan
+    // computes it, times N^-1
+    const uint32_t w1 = pow_mod(pow_mod(d.psi.v[r], 2 * d.N - 1, q), d.N / 2, q);
+    a.w1n[r] = (uint32_t)((uint64_t)w1 * d.ninv[r] % q);
+    a.w1n_q[r] = (uint32_t)(((uint64_t)a.w1n[r] << 32) / q);
+    lazy = lazy && q <= (1u << 29);
   }
   timer_mark_start(stream);
   hipError_t e = hipErrorInvalidValue;
   switch (d.logn) {
-    case 4: e = launch_for<4>(a, mode, stream); break;
-    case 5: e = launch_for<5>(a, mode, stream); break;
-    case 6: e = launch_for<6>(a, mode, stream); break;
-    case 7: e = launch_for<7>(a, mode, stream); break;
-    case 8: e = launch_for<8>(a, mode, stream); break;
-    case 9: e = launch_for<9>(a, mode, stream); break;
-    case 10: e = launch_for<10>(a, mode, stream); break;
-    case 11: e = launch_for<11>(a, mode, stream); break;
-    case 12: e = launch_for<12>(a, mode, stream); break;
-    case 13: e = launch_for<13>(a, mode, stream); break;
+    case 4: e = launch_for<4>(a, lazy, mode, stream); break;
+    case 5: e = launch_for<5>(a, lazy, mode, stream); break;
+    case 6: e = launch_for<6>(a, lazy, mode, stream); break;
+    case 7: e = launch_for<7>(a, lazy, mode, stream); break;
+    case 8: e = launch_for<8>(a, lazy, mode, stream); break;
+    case 9: e = launch_for<9>(a, lazy, mode, stream); break;
+    case 10: e = launch_for<10>(a, lazy, mode, stream); break;
+    case 11: e = launch_for<11>(a, lazy, mode, stream); break;
+    case 12: e = launch_for<12>(a, lazy, mode, stream); break;
+    case 13: e = launch_for<13>(a, lazy, mode, stream); break;
     default: break;
   }
   timer_mark_stop(stream);

@@ -34,12 +34,15 @@ def primes_for(N, R, bits=30):
     return oracle.ntt_primes(bits, 2 * N, R)
 
 
+@pytest.mark.parametrize("bits", [30, 29])
 @pytest.mark.parametrize("logn", list(range(4, 14)))
-def test_every_degree_forward_inverse_rns(logn):
+def test_every_degree_forward_inverse_rns(logn, bits):
+    """Primes just below 2^30 (residues kept below 4q) and below 2^29 (the
+    looser bounds that 8q < 2^32 allows)."""
     import torch
 
     N = 1 << logn
-    q = primes_for(N, 3)
+    q = primes_for(N, 3, bits=bits)
     count = 3 if N >= 4096 else 5
     say(f"ntt N={N} q={q} count={count}")
     shape, plan, psis = make_plan(N, q)
