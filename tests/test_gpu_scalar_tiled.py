@@ -74,12 +74,32 @@ def test_tiled_shapes_full(M, K, B):
     np.testing.assert_array_equal(run_gpu(db, Q), oracle.scalar(db, Q))
 
 
+def wide_random_shapes(n=8, seed=2027):
+    """Seeded random shapes for the wide launches: B from 65 to 700 (one to
+    five 128-column groups, partial groups and narrow remainders), ragged M and
+    K, at most 4e8 multiply-adds each for the oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M, K, B = int(rng.integers(1, 700)), int(rng.integers(1, 6000)), int(rng.integers(65, 701))
+        if M * K * B <= 4e8:
+            out.append((M, K, B))
+    return out
+
+
+@pytest.mark.parametrize("M,K,B", wide_random_shapes())
+def test_tiled_wide_random(M, K, B):
+    say(f"scalar tiled wide M={M} K={K} B={B}")
+    db, Q = rand_case(M * 7 + K * 3 + B, M, K, B)
+    np.testing.assert_array_equal(run_gpu(db, Q), oracle.scalar(db, Q))
+
+
 def test_tiled_from_misaligned_source():
     db, Q = rand_case(4, 40, 4096, 3)
     np.testing.assert_array_equal(run_gpu(db, Q, offset=5), oracle.scalar(db, Q))
 
 
-@pytest.mark.parametrize("B", [1, 32])
+@pytest.mark.parametrize("B", [1, 32, 200])
 def test_tiled_overflow_closed_forms(B):
     """db = -128, Q = 0x80808080 (digits -128, -127, -127, -127): every digit
     plane's int32 sum passes 2^31 in one accumulator at K = 2^17."""
