@@ -108,43 +108,55 @@ __device__ __forceinline__ void limb_fragments(const uint32_t w[16], v4i f[4]) {
 // and k past K give zero bytes.
 // ---------------------------------------------------------------------------
 
-// One workgroup per (32 points, k-group lg, tile t, step s): the tile's 16
-// rows x 16 k are read as 256 runs of 32 points (128 contiguous bytes each)
-// into LDS, then each thread forms the fragment lanes of points p: 16 words
-// -> centred signed limbs -> 4 x 16 bytes.  Needs P % 4 == 0, a 16-byte
-// aligned source and strides that are multiples of 4 words.
-// LDS word of (row r, point p): r*32 + ((p + 4*(r/16)) mod 32), which keeps
+// One workgroup per (32 points, tile t, `sub` consecutive (step s, k-group
+// lg) pairs): 16 row slots x 16 k are read as 256 runs of 32 points (128
+// contiguous bytes each) into LDS, then each thread forms the fragment lanes
+// of points p: 16 words -> centred signed limbs -> 4 x 16 bytes.  With
+// lpg = 16 a slot is a row of the tile and sub = 1; a small batch's compact
+// packing (lpg < 16 live rows) gives slot = j * lpg2 + row (lpg2 = lpg
+// rounded up to a power of two) to sub = 16 / lpg2 pairs, so every slot
+// holds live rows.  Pair index u * sub + j is lg + 4s.  Needs P % 4 == 0, a
+// 16-byte aligned source and strides that are multiples of 4 words.
+// LDS word of (slot r, point p): r*32 + ((p + 4*(r/16)) mod 32), which keeps
 // both the 16-byte row stores and the per-thread column reads at two-way
 // bank conflicts at most.
 constexpr int kPackPoints = 32;
+__host__ __device__ __forceinline__ uint32_t pack_lpg2(uint32_t lpg) {
+  uint32_t v = 1;
+  while (v < lpg) v <<= 1;
+  return v;  // lpg in [1, 16]
+}
+
 __global__ __launch_bounds__(kThreads) void pack_limbs4_kernel(PackDesc d, uint64_t pblocks, uint64_t total) {
   __shared__ uint32_t tile[256 * kPackPoints];
   const uint32_t tid = threadIdx.x;
+  const uint32_t lpg2 = pack_lpg2(d.lpg), sub = 16 / lpg2, pairs = 4 * d.S;
   for (uint64_t id = blockIdx.x; id < total; id += gridDim.x) {
     const uint64_t pb = id % pblocks;
-    uint64_t rest = id / pblocks;
-    const uint32_t lg = (uint32_t)(rest % 4);
-    rest /= 4;
+    const uint64_t rest = id / pblocks;
     const uint32_t t = (uint32_t)(rest % d.tiles);
-    const uint32_t s = (uint32_t)(rest / d.tiles);
+    const uint32_t u = (uint32_t)(rest / d.tiles);
     const uint64_t p0 = pb * kPackPoints;
     __syncthreads();  // the previous item's reads of `tile` are done
 #pragma unroll
     for (int pass = 0; pass < 8; ++pass) {
       const uint32_t r = pass * 32 + tid / 8, c4 = (tid % 8) * 4;
-      const uint64_t row = (uint64_t)d.row_base + t * 16 + r / 16;
-      const uint32_t k = s * 64 + lg * 16 + r % 16;
+      const uint32_t slot = r / 16, rr = slot % lpg2, pr = u * sub + slot / lpg2;
+      const uint64_t row = (uint64_t)d.row_base + t * 16 + rr;
+      const uint32_t k = (pr / 4) * 64 + (pr % 4) * 16 + r % 16;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < d.rows && k < d.K && p0 + c4 < d.P)
+      if (rr < d.lpg && pr < pairs && row < d.rows && k < d.K && p0 + c4 < d.P)
         v = *reinterpret_cast<const uint4*>(d.src + row * d.s_row + (uint64_t)k * d.s_k + p0 + c4);
       *reinterpret_cast<uint4*>(&tile[r * kPackPoints + ((c4 + 4 * (r / 16)) % kPackPoints)]) = v;
     }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t li = tid % 16, pp = h * 16 + tid / 16;
+      const uint32_t li = tid % 16, pp = h * 16 + tid / 16;  // li: the slot
+      const uint32_t rr = li % lpg2, pr = u * sub + li / lpg2;
       const uint64_t p = p0 + pp;
-      if (p >= d.P || li >= d.lpg) continue;
+      if (p >= d.P || rr >= d.lpg || pr >= pairs) continue;
+      const uint32_t s = pr / 4, lg = pr % 4;
       const uint32_t q = d.q[p / d.N], half = q / 2;
       uint32_t w[16];
 #pragma unroll
@@ -154,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void pack_limbs4_kernel(PackDesc d, uint6
       v4i f[4];
       limb_fragments(w, f);
       v4i* dst = static_cast<v4i*>(d.dst) + p * d.d_p + (t / d.tgroup) * d.d_g + (t % d.tgroup) * d.d_t +
-                 s * d.d_s + lg * d.lpg + li;
+                 s * d.d_s + lg * d.lpg + rr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[j * 4 * d.lpg] = f[j];
     }
@@ -612,7 +624,8 @@ hipError_t launch_pack(const PackDesc& d, hipStream_t stream) {
   auto a16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
   if (d.P % 4 == 0 && d.s_row % 4 == 0 && d.s_k % 4 == 0 && a16(d.src)) {
     const uint64_t pblocks = (d.P + kPackPoints - 1) / kPackPoints;
-    const uint64_t total = pblocks * 4 * d.tiles * d.S;
+    const uint32_t sub = 16 / pack_lpg2(d.lpg);
+    const uint64_t total = pblocks * d.tiles * ((4ull * d.S + sub - 1) / sub);
     const uint64_t grid = total < (1ull << 20) ? total : (1ull << 20);
     hipLaunchKernelGGL(pack_limbs4_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, d, pblocks, total);
   } else {
