@@ -508,9 +508,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(const int8_t* __r
 // 0..3 of query columns 16w..16w+15 of its group (one column tile per plane),
 // 32 accumulator tiles.  The column groups of one row block are neighbouring
 // tiles, run side by side on one XCD: the first to read a DB fragment brings
-// it into that XCD's L2 for the others.  (Under sustained matrix load the
-// chip's clock is held by its power budget; the HBM reads saved this way
-// raise it.)
+// it into that XCD's L2 for the others.  (The clock the chip holds during
+// these passes falls with their HBM and L2 traffic; the HBM reads saved
+// this way raise it.)
 //  * DB fragments (the A operand, used by all 8 waves) come into a six-step
 //    LDS ring once per workgroup with direct global-to-LDS loads, one 1 KiB
 //    fragment per wave per step, four steps ahead.
