@@ -133,17 +133,24 @@ def test_tiled_one_hot_and_regev_view():
 
 def test_tiled_hint_and_second_fold_sampled():
     """VIPIR's offline hint (the 2^20 x 2^16 database view times the
-    2^16 x 1280 matrix A: 20 passes of 64 query columns) and the double-packing
-    second fold (32768 x 2^17 times 2^17 x 1281) on tiled copies of the 64 GiB
-    database's leading bytes, as the benchmark runs them."""
+    2^16 x 1280 matrix A: wide launches of four, four and two 128-column
+    groups) and the double-packing second fold (32768 x 2^17 times
+    2^17 x 1281: the same plus one narrow column, K split in four blocks) on
+    tiled copies of the 64 GiB database's leading bytes, as the benchmark runs
+    them.  Sampled rows: two in each eighth of the rows (each XCD's share of
+    the hint's first launch) and the first and last row; every column."""
     import torch
 
     seed, N_LWE = 5, 1280
     say("scalar tiled hint / second fold: synthesising 64 GiB")
     d_bytes = torch.empty(1 << 36, dtype=torch.int8, device="cuda:0")
     synth.fill_int8_(d_bytes, seed, synth.STREAM_SCALAR_DB)
-    for M, K, B, rows, qseed in (((1 << 20), (1 << 16), N_LWE, [0, 777, (1 << 20) - 1], seed + 100),
-                                 (32768, 1 << 17, N_LWE + 1, [0, 4097, 32767], seed + 200)):
+    def spread(M):
+        eighth = M // 8
+        return sorted({0, M - 1} | {x * eighth + o for x in range(8) for o in (5, eighth // 2 + 77)})
+
+    for M, K, B, rows, qseed in (((1 << 20), (1 << 16), N_LWE, spread(1 << 20), seed + 100),
+                                 (32768, 1 << 17, N_LWE + 1, spread(32768), seed + 200)):
         say(f"  M={M} K={K} B={B}")
         t = tiled(d_bytes[:M * K].view(M, K))
         d_q = empty_u32((K, B))
