@@ -165,3 +165,36 @@ def test_section_3_6_size_every_output():
         release()
     del d_h, d_ht
     release()
+
+
+def random_exppack_cases(n=8, seed=5003):
+    """Seeded random ExpPack cases: N from 16 to 256, one to three moduli
+    below 2^31 (or, one case in four, at or above 2^31: the VALU scan), Dr and
+    n up to 300, B up to 20 (2B rows: multi-pass past 32), G present or
+    absent, at most 1.5e8 multiply-adds each for the oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        N = 1 << int(rng.integers(4, 9))
+        R = int(rng.integers(1, 4))
+        wide = bool(rng.integers(0, 4) == 0)
+        lo, hi = (1 << 31, 1 << 32) if wide else (2, 1 << 31)
+        q = [int(v) for v in rng.integers(lo, hi, size=R, dtype=np.uint64)]
+        Dr, n_, B = int(rng.integers(1, 301)), int(rng.integers(1, 301)), int(rng.integers(1, 21))
+        if Dr * n_ * 2 * B * N * R <= 1.5e8:
+            out.append((N, tuple(q), Dr, n_, B, bool(rng.integers(0, 2)), int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("N,q,Dr,n,B,with_g,s", random_exppack_cases())
+def test_random_shapes_both_scans(N, q, Dr, n, B, with_g, s):
+    q = list(q)
+    P = N * len(q)
+    rng = np.random.default_rng(s)
+    say(f"exppack random N={N} R={len(q)} Dr={Dr} n={n} B={B} G={with_g}")
+    H = rand_res(rng, (Dr, n, P), N, q)
+    C = rand_res(rng, (n, 2 * B, P), N, q)
+    G = rand_res(rng, (Dr, B, P), N, q) if with_g else None
+    want = oracle.exppack(H, C, G, N, q)
+    np.testing.assert_array_equal(run_gpu(H, C, G, N, q), want)
+    np.testing.assert_array_equal(run_gpu(H, C, G, N, q, scan=pirscan.SCAN_VALU), want)

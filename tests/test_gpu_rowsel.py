@@ -254,3 +254,35 @@ def test_limb_diagonals_at_the_largest_reduction(m):
         ct = np.where(rng.integers(0, 2, size=(m, D0, P)) == 1, xneg, xpos).astype(np.uint32)
         db = np.where(rng.integers(0, 2, size=(D0, D1, P)) == 1, xneg, xpos).astype(np.uint32)
         np.testing.assert_array_equal(run_gpu(ct, db, N, q), oracle.rowsel(ct, db, N, q))
+
+
+def random_rowsel_cases(n=10, seed=4099):
+    """Seeded random RowSel cases: N a power of two from 16 to 512, R from 1
+    to 4 limbs with moduli drawn from [2, 2^31) (the int8 scan) or [2^31,
+    2^32) (the VALU scan), D0 up to 300, D1 up to 300, m up to 40 (multi-pass
+    past 32), at most 1.5e8 multiply-adds each for the oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        N = 1 << int(rng.integers(4, 10))
+        R = int(rng.integers(1, 5))
+        wide = bool(rng.integers(0, 4) == 0)
+        lo, hi = (1 << 31, 1 << 32) if wide else (2, 1 << 31)
+        q = [int(v) for v in rng.integers(lo, hi, size=R, dtype=np.uint64)]
+        D0, D1, m = int(rng.integers(1, 301)), int(rng.integers(1, 301)), int(rng.integers(1, 41))
+        if m * D0 * D1 * N * R <= 1.5e8:
+            out.append((N, tuple(q), D0, D1, m, int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("N,q,D0,D1,m,s", random_rowsel_cases())
+def test_random_shapes_both_scans(N, q, D0, D1, m, s):
+    q = list(q)
+    P = N * len(q)
+    rng = np.random.default_rng(s)
+    say(f"rowsel random N={N} R={len(q)} D0={D0} D1={D1} m={m}")
+    ct = rand_res(rng, (m, D0, P), N, q)
+    db = rand_res(rng, (D0, D1, P), N, q)
+    want = oracle.rowsel(ct, db, N, q)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, q), want)
+    np.testing.assert_array_equal(run_gpu(ct, db, N, q, scan=pirscan.SCAN_VALU), want)
